@@ -1,0 +1,228 @@
+/*
+ * lora_sgmv.h — C ABI of the MI355X (gfx950) segment-routed multi-adapter
+ * LoRA delta:  y[t] += B[slot(t)] · (A[slot(t)] · x[t]).
+ *
+ * The delta is computed in two steps over a batch whose requests are sorted
+ * by adapter slot: an SGMV "shrink" (x -> rank-space intermediate u) and a
+ * boundary-aware "expand" (u -> the output slices of a fused q/k/v projection,
+ * or of o_proj).  Both are driven by the routing triple (lora_ids,
+ * grouped_offsets, end).
+ *
+ * Sources (by page title and section):
+ *   [MAX-lora]  "MAX 的 max.pipelines.lora 模块解析" — LoRAConfig table;
+ *               LoRAModel "加载时的处理管线" (validate, pre-scale, pad, fuse
+ *               QKV, cast); "运行时工作流与调度交互" (base-only routing);
+ *               LoRAStatus table.
+ *   [MAX-V3]    Modular API page "LoRAManagerV3" — sort_lora_batch(),
+ *               get_lora_graph_inputs(), bind_inputs() errors.
+ *   [vLLM]      "vLLM LoRA 实现深度解析" — §1 (forward, scaling, rsLoRA,
+ *               pre-multiplied scaling), §5.3 (activate_adapter, reset_lora),
+ *               §6 (lora_shrink / lora_expand), §9 (stacked buffer layout).
+ *
+ * Conventions for every entry point
+ *   - Return value: a lora_status_t code (0 = success).  No call throws,
+ *     aborts or prints.  Arguments are checked before any work or launch; on
+ *     an error nothing is written and nothing is launched.
+ *   - Memory: the caller owns every buffer.  The library allocates no memory
+ *     and keeps no pointer after a call returns.  Host calls take host
+ *     pointers; device calls take device pointers (HBM) and run
+ *     asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Layout: row-major, no padding between elements of a row; a row stride
+ *     (ld*) in elements where stated.  bf16 data is passed as 16-bit patterns.
+ *   - Thread safety: host calls are re-entrant.  Device calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef LORA_SGMV_H
+#define LORA_SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+/* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
+ * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
+ * ValueError cases the pages name (bad rank/bias/target, no free slot, input
+ * count mismatch). */
+typedef int32_t lora_status_t;
+enum {
+    LORA_OK = 0,                    /* success */
+    LORA_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size/stride/dtype/family/path, bad offsets, misalignment */
+    LORA_ERR_INVALID_ADAPTER = 2,   /* rank < 1 or > max_lora_rank, bias not "none", unknown target */
+    LORA_ERR_SLOT_OUT_OF_RANGE = 3, /* slot id outside [-1, max_num_loras) */
+    LORA_ERR_CAPACITY = 4,          /* a caller buffer (workspace, output) is too small */
+    LORA_ERR_DEVICE = 5,            /* the HIP runtime reported an error for a launch */
+    LORA_ERR_UNSPECIFIED = 6        /* anything else */
+};
+
+/* Element type of x, y and the adapter stacks.  Accumulation is always fp32. */
+enum { LORA_DTYPE_F32 = 0, LORA_DTYPE_BF16 = 1 };
+
+/* Projection families.  QKV: input width hidden, three output slices of
+ * widths (n_heads*head_dim, n_kv_heads*head_dim, n_kv_heads*head_dim).
+ * O: input width n_heads*head_dim, one output slice of width hidden.
+ * ([MAX-lora] LoRATargetModule: fused self_attn.qkv = (q,k,v)_proj; o_proj.) */
+enum { LORA_FAMILY_QKV = 0, LORA_FAMILY_O = 1 };
+
+/* Adapter target bits (q_proj, k_proj, v_proj, o_proj). */
+enum { LORA_TARGET_Q = 1, LORA_TARGET_K = 2, LORA_TARGET_V = 4, LORA_TARGET_O = 8 };
+
+/* Kernel path selection for the device calls.  AUTO picks per token tile:
+ * wavefront-reduction VALU code for short (decode-shaped) tiles, MFMA for
+ * longer bf16 tiles.  VALU / MFMA force one path (MFMA needs bf16, a rank that
+ * is a multiple of 16 and slice widths that are multiples of 16). */
+enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2 };
+
+/* Model and LoRA capacity dimensions.  max_lora_rank (R) and max_num_loras (L)
+ * correspond to LoRAConfig.max_lora_rank / max_num_loras ([MAX-lora] LoRAConfig
+ * table; page defaults 16 and 1).  Constraints checked by every call:
+ * all fields > 0; hidden, n_heads*head_dim and n_kv_heads*head_dim multiples
+ * of 8; max_lora_rank a multiple of 8 and <= 512; dtype one of LORA_DTYPE_*. */
+typedef struct lora_dims {
+    int32_t hidden;
+    int32_t n_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t max_lora_rank;
+    int32_t max_num_loras;
+    int32_t dtype;
+} lora_dims_t;
+
+/* Library ABI version (LORA_ABI_VERSION of the build). */
+int32_t lora_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("LORA_OK", ...). */
+const char* lora_status_string(lora_status_t status);
+
+/* Shape of a projection family: input width, slice count (1..4), the slice
+ * widths (slice_widths needs room for 4 entries) and the total output width.
+ * The packed stacks of the family are A [L][n_slices*R][in_features] and
+ * B [L][out_features][R]. */
+lora_status_t lora_family_shape(const lora_dims_t* dims, int32_t family, int32_t* in_features,
+                                int32_t* n_slices, int32_t* slice_widths, int32_t* out_features);
+
+/* ---------------------------------------------------------------------------
+ * lora_pack_adapter — host, synchronous.
+ *
+ * Turns one adapter's per-projection PEFT matrices of one layer into one slot
+ * of the layer's stacks, in the page's order ([MAX-lora] 加载时的处理管线;
+ * [vLLM] §1 pre-multiplied scaling, §5.3 reset_lora, §5.4 packed qkv):
+ *   1. validate: bias_none != 0, 1 <= rank <= max_lora_rank, target_mask
+ *      within Q|K|V|O  (else LORA_ERR_INVALID_ADAPTER);
+ *   2. scale = lora_alpha / rank, or lora_alpha / sqrt(rank) when use_rslora;
+ *      B <- fp32(B * fp32(scale)) (one fp32 multiply per element);
+ *   3. zero-pad A [rank, in] -> [R, in] and B [out, rank] -> [out, R];
+ *   4. fuse q/k/v: A_qkv = [A_q; A_k; A_v] (rank dim), B_qkv = [B_q; B_k; B_v]
+ *      (output dim);
+ *   5. cast to dims->dtype with round-to-nearest-even (bf16) or keep fp32.
+ * A projection not in target_mask gets all-zero blocks (its delta is zero).
+ *
+ * Inputs: A_p [rank][in_p] and B_p [out_p][rank] fp32, row-major, for the
+ * targeted projections (NULL allowed for the others); in_q = in_k = in_v =
+ * hidden, in_o = n_heads*head_dim; out_q = n_heads*head_dim, out_k = out_v =
+ * n_kv_heads*head_dim, out_o = hidden.
+ * Outputs (host memory, dims->dtype): A_qkv [3R][hidden],
+ * B_qkv [nq+2nkv][R], A_o [R][nq], B_o [hidden][R] — one slot each; the
+ * caller copies them into slot s of the device stacks.
+ */
+lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lora_alpha,
+                                int32_t use_rslora, int32_t bias_none, uint32_t target_mask,
+                                const float* A_q, const float* B_q, const float* A_k,
+                                const float* B_k, const float* A_v, const float* B_v,
+                                const float* A_o, const float* B_o, void* A_qkv_out,
+                                void* B_qkv_out, void* A_o_out, void* B_o_out);
+
+/* ---------------------------------------------------------------------------
+ * lora_build_routing — host, synchronous.
+ *
+ * [MAX-V3] sort_lora_batch(): requests of one adapter adjacent, ordered by
+ * slot id, base requests (slot -1) last; order within a slot is arrival order
+ * (stable).  [MAX-V3] get_lora_graph_inputs(): consecutive same-slot requests
+ * form a group; grouping stops at the first base request; `end` is the
+ * number of LoRA-routed tokens.  Requests with zero tokens keep their place
+ * (a group may be empty).
+ *
+ * Inputs:  request_slot[num_requests] in [-1, max_num_loras);
+ *          row_offsets[num_requests+1], row_offsets[0] == 0, non-decreasing,
+ *          request i owns tokens [row_offsets[i], row_offsets[i+1]).
+ * Outputs: perm[num_requests] (sorted position -> arrival index),
+ *          sorted_row_offsets[num_requests+1],
+ *          lora_ids[G] (capacity max_num_loras), grouped_offsets[G+1]
+ *          (capacity max_num_loras+1; [0] = 0, [G] = end; token offsets in the
+ *          sorted batch), *num_groups = G, *end.
+ * Errors:  LORA_ERR_SLOT_OUT_OF_RANGE for a bad slot; LORA_ERR_INVALID_ARGUMENT
+ *          for bad offsets, null pointers or end >= 2^31.
+ * A base-only or empty batch gives G = 0, end = 0; the device calls then do
+ * nothing.
+ */
+lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
+                                 const int64_t* row_offsets, int32_t max_num_loras,
+                                 int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,
+                                 int32_t* grouped_offsets, int32_t* num_groups, int64_t* end);
+
+/* Workspace bytes lora_sgmv_shrink needs for a family, for any batch with at
+ * most max_tokens LoRA-routed tokens and at most dims->max_num_loras groups.
+ * The workspace must be zero-filled before its first use; every completed
+ * shrink leaves its counter area zero again, so it can be reused as is. */
+lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
+                                        int64_t max_tokens, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * lora_sgmv_shrink — device, asynchronous on `stream`.
+ *
+ * [vLLM] §6 lora_shrink (A·x, hidden -> rank) over the segments of the
+ * routing triple ([MAX-V3] get_lora_graph_inputs):
+ *   u[t][c] = sum_k A[lora_ids[g]][c][k] * x[t][k]
+ *   for t in [grouped_offsets[g], grouped_offsets[g+1]), g < num_groups,
+ *   c < n_slices*R, accumulated in fp32.
+ *
+ * x        [>= end rows][in_features] in dims->dtype, row stride ldx elements;
+ *          rows >= end are not read.
+ * A_stack  [L][n_slices*R][in_features] in dims->dtype (the family's packed stack).
+ * lora_ids, grouped_offsets: device int32 arrays of num_groups and
+ *          num_groups+1 entries as produced by lora_build_routing.
+ * u        fp32 [end][n_slices*R] (device).
+ * workspace: device, >= lora_sgmv_workspace_bytes(dims, family, end), zero-filled
+ *          before first use; NULL allowed when the call needs none.
+ * path     LORA_PATH_*.
+ * Alignment: x, A_stack, u and workspace 16-byte aligned; ldx*element size a
+ * multiple of 16.  Malformed device routing cannot make the kernel access
+ * memory outside [0, end) rows or the stacks (indices are clamped and bad
+ * slot ids skipped), but the result is then unspecified.
+ */
+lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
+                               const void* A_stack, const int32_t* lora_ids,
+                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
+                               float* u, void* workspace, size_t workspace_bytes, int32_t path,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lora_sgmv_expand — device, asynchronous on `stream`.
+ *
+ * [vLLM] §6 lora_expand (B·u, rank -> hidden), boundary-aware ([MAX-V3]
+ * get_lora_graph_inputs: `end` bounds the rows the expand touches):
+ *   y[t][off_s + o] = round(y[t][off_s + o] + sum_j B[lora_ids[g]][off_s + o][j] * u[t][s*R + j])
+ *   for t < end in segment g, slice s with offset off_s, fp32 accumulation and
+ *   one rounding to dims->dtype (round to nearest even).  Rows >= end are
+ *   neither read nor written.
+ *
+ * u        fp32 [end][n_slices*R] (device), as lora_sgmv_shrink wrote it.
+ * B_stack  [L][out_features][R] in dims->dtype.
+ * y        [>= end rows][out_features] in dims->dtype, row stride ldy, updated in place.
+ * Alignment: u, B_stack and y 16-byte aligned; ldy*element size a multiple of 16.
+ * u must not alias y.
+ */
+lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
+                               const void* B_stack, const int32_t* lora_ids,
+                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
+                               void* y, int64_t ldy, int32_t path, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_SGMV_H */

@@ -1,0 +1,33 @@
+"""Python binding of the MI355X segment-routed multi-adapter LoRA delta library.
+
+Argument marshalling only: every step runs in liblora_sgmv.so (host C++ for
+packing and routing, HIP kernels for shrink and expand).  There is no
+fallback: if the library is not built, importing the device functions raises.
+
+Host functions take and return numpy arrays.  Device functions take torch
+tensors that live on the GPU and launch on torch's current stream (or the
+stream passed in).
+"""
+
+from ._lib import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    FAMILY_O,
+    FAMILY_QKV,
+    PATH_AUTO,
+    PATH_MFMA,
+    PATH_VALU,
+    LoraDims,
+    LoraError,
+    family_shape,
+    library_path,
+    lora_abi_version,
+    lora_build_routing,
+    lora_family_shape,
+    lora_pack_adapter,
+    lora_sgmv_expand,
+    lora_sgmv_shrink,
+    lora_sgmv_workspace_bytes,
+    lora_status_string,
+    packed_to_torch,
+)

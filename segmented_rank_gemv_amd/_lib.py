@@ -1,0 +1,253 @@
+"""ctypes declarations of include/lora_sgmv.h and thin wrappers with the same names."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "liblora_sgmv.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+FAMILY_QKV, FAMILY_O = 0, 1
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+_TARGET_BITS = {"q": 1, "k": 2, "v": 4, "o": 8}
+_DTYPES = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
+
+
+class LoraError(Exception):
+    """A non-zero lora_status_t.  Codes 1-4 (bad argument, invalid adapter,
+    slot out of range, capacity) also derive from ValueError."""
+
+    def __init__(self, code: int, name: str, where: str):
+        super().__init__(f"{where}: {name} ({code})")
+        self.code = code
+        self.name = name
+
+
+class _LoraValueError(LoraError, ValueError):
+    pass
+
+
+class _LoraDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_lora_rank", ctypes.c_int32), ("max_num_loras", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class LoraDims:
+    """Model and LoRA capacity dimensions.  The defaults of max_lora_rank and
+    max_num_loras are the pages' LoRAConfig defaults (16 and 1)."""
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    max_lora_rank: int = 16
+    max_num_loras: int = 1
+    dtype: str = "bf16"
+
+    def c(self) -> _LoraDims:
+        return _LoraDims(self.hidden, self.n_heads, self.n_kv_heads, self.head_dim,
+                         self.max_lora_rank, self.max_num_loras, _DTYPES[self.dtype])
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run segmented_rank_gemv_amd.build.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    D = ctypes.POINTER(_LoraDims)
+    lib.lora_abi_version.restype = i32
+    lib.lora_abi_version.argtypes = []
+    lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_status_string.argtypes = [i32]
+    lib.lora_family_shape.restype = i32
+    lib.lora_family_shape.argtypes = [D, i32, P, P, P, P]
+    lib.lora_pack_adapter.restype = i32
+    lib.lora_pack_adapter.argtypes = [D, i32, ctypes.c_float, i32, i32, u32] + [P] * 12
+    lib.lora_build_routing.restype = i32
+    lib.lora_build_routing.argtypes = [i32, P, P, i32, P, P, P, P, P, P]
+    lib.lora_sgmv_workspace_bytes.restype = i32
+    lib.lora_sgmv_workspace_bytes.argtypes = [D, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lora_sgmv_shrink.restype = i32
+    lib.lora_sgmv_shrink.argtypes = [D, i32, P, i64, P, P, P, i32, i64, P, P, ctypes.c_size_t,
+                                     i32, P]
+    lib.lora_sgmv_expand.restype = i32
+    lib.lora_sgmv_expand.argtypes = [D, i32, P, P, P, P, i32, i64, P, i64, i32, P]
+    _lib = lib
+    return lib
+
+
+def lora_status_string(code: int) -> str:
+    return _load().lora_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        name = lora_status_string(code)
+        cls = _LoraValueError if 1 <= code <= 4 else LoraError
+        raise cls(code, name, where)
+
+
+def lora_abi_version() -> int:
+    return int(_load().lora_abi_version())
+
+
+def _np_ptr(a: Optional[np.ndarray]) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+# ----------------------------------------------------------------------------- host
+def lora_family_shape(dims: LoraDims, family: int) -> Tuple[int, int, Tuple[int, ...], int]:
+    """(in_features, n_slices, slice_widths, out_features)."""
+    i = np.zeros(1, np.int32)
+    n = np.zeros(1, np.int32)
+    w = np.zeros(4, np.int32)
+    o = np.zeros(1, np.int32)
+    dc = dims.c()
+    _check(_load().lora_family_shape(ctypes.byref(dc), family, _np_ptr(i), _np_ptr(n), _np_ptr(w),
+                                     _np_ptr(o)), "lora_family_shape")
+    return int(i[0]), int(n[0]), tuple(int(v) for v in w[:int(n[0])]), int(o[0])
+
+
+family_shape = lora_family_shape
+
+
+def lora_pack_adapter(dims: LoraDims, rank: int, lora_alpha: float, use_rslora: bool,
+                      bias_none: bool, targets: Sequence[str],
+                      weights: Dict[str, Tuple[np.ndarray, np.ndarray]],
+                      target_mask: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Pack one adapter of one layer; returns host arrays A_qkv, B_qkv, A_o,
+    B_o (uint16 bf16 patterns or float32)."""
+    R = dims.max_lora_rank
+    nq, nkv = dims.n_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    st = np.uint16 if dims.dtype == "bf16" else np.float32
+    out = {"A_qkv": np.empty((3 * R, dims.hidden), st), "B_qkv": np.empty((nq + 2 * nkv, R), st),
+           "A_o": np.empty((R, nq), st), "B_o": np.empty((dims.hidden, R), st)}
+    if target_mask is None:
+        target_mask = 0
+        for t in targets:
+            target_mask |= _TARGET_BITS[t]
+    keep = []
+    ptrs = []
+    for i, p in enumerate("qkvo"):
+        if (target_mask >> i) & 1 and p in weights:
+            a = np.ascontiguousarray(weights[p][0], dtype=np.float32)
+            b = np.ascontiguousarray(weights[p][1], dtype=np.float32)
+            keep += [a, b]
+            ptrs += [_np_ptr(a), _np_ptr(b)]
+        else:
+            ptrs += [None, None]
+    dc = dims.c()
+    _check(_load().lora_pack_adapter(ctypes.byref(dc), int(rank), float(lora_alpha),
+                                     int(bool(use_rslora)), int(bool(bias_none)), int(target_mask),
+                                     *ptrs, _np_ptr(out["A_qkv"]), _np_ptr(out["B_qkv"]),
+                                     _np_ptr(out["A_o"]), _np_ptr(out["B_o"])),
+           "lora_pack_adapter")
+    return out
+
+
+def lora_build_routing(request_slot: np.ndarray, row_offsets: np.ndarray,
+                       max_num_loras: int) -> Dict[str, object]:
+    slots = np.ascontiguousarray(request_slot, dtype=np.int32)
+    offs = np.ascontiguousarray(row_offsets, dtype=np.int64)
+    n = slots.size
+    if offs.size != n + 1:
+        raise ValueError("row_offsets must have num_requests + 1 entries")
+    L = int(max_num_loras)
+    perm = np.zeros(max(n, 1), np.int32)
+    srt = np.zeros(n + 1, np.int64)
+    ids = np.zeros(max(L, 1), np.int32)
+    goffs = np.zeros(max(L, 1) + 1, np.int32)
+    G = np.zeros(1, np.int32)
+    end = np.zeros(1, np.int64)
+    _check(_load().lora_build_routing(n, _np_ptr(slots), _np_ptr(offs), L, _np_ptr(perm),
+                                      _np_ptr(srt), _np_ptr(ids), _np_ptr(goffs), _np_ptr(G),
+                                      _np_ptr(end)), "lora_build_routing")
+    g = int(G[0])
+    return {"perm": perm[:n].copy(), "sorted_offsets": srt, "lora_ids": ids[:g].copy(),
+            "grouped_offsets": goffs[:g + 1].copy(), "num_groups": g, "end": int(end[0])}
+
+
+def lora_sgmv_workspace_bytes(dims: LoraDims, family: int, max_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    dc = dims.c()
+    _check(_load().lora_sgmv_workspace_bytes(ctypes.byref(dc), family, int(max_tokens),
+                                             ctypes.byref(out)), "lora_sgmv_workspace_bytes")
+    return int(out.value)
+
+
+# ----------------------------------------------------------------------------- device
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev_ptr(t, what: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def _row_stride(t, what: str) -> int:
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be a 2-D tensor")
+    if t.numel() == 0:
+        return int(t.shape[1])
+    if t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit column stride")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.stride(0), t.shape[1]))
+
+
+def lora_sgmv_shrink(dims: LoraDims, family: int, x, A_stack, lora_ids, grouped_offsets,
+                     num_groups: int, end: int, u, workspace=None, path: int = PATH_AUTO,
+                     stream=None) -> None:
+    """u[:end] = per-segment A[slot] . x (fp32), asynchronously on the stream."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dc = dims.c()
+    _check(_load().lora_sgmv_shrink(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
+                                     _dev_ptr(A_stack, "A_stack"), _dev_ptr(lora_ids, "lora_ids"),
+                                     _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
+                                     int(end), _dev_ptr(u, "u"), _dev_ptr(workspace, "workspace"),
+                                     ws_bytes, int(path), _stream_handle(stream)),
+           "lora_sgmv_shrink")
+
+
+def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, lora_ids, grouped_offsets,
+                     num_groups: int, end: int, y, path: int = PATH_AUTO, stream=None) -> None:
+    """y[:end] += per-segment B[slot] . u, in place, asynchronously on the stream."""
+    dc = dims.c()
+    _check(_load().lora_sgmv_expand(ctypes.byref(dc), family, _dev_ptr(u, "u"),
+                                     _dev_ptr(B_stack, "B_stack"), _dev_ptr(lora_ids, "lora_ids"),
+                                     _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
+                                     int(end), _dev_ptr(y, "y"), _row_stride(y, "y"), int(path),
+                                     _stream_handle(stream)),
+           "lora_sgmv_expand")
+
+
+def packed_to_torch(a: np.ndarray):
+    """Host packed array (uint16 bf16 patterns or float32) -> CPU torch tensor of
+    the matching dtype, sharing no memory with `a`."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).copy())

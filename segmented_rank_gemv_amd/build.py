@@ -1,0 +1,51 @@
+"""Build step of the HIP library: one hipcc call for gfx950, in-tree.
+
+    python -m segmented_rank_gemv_amd.build
+"""
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "liblora_sgmv.so")
+SOURCES = [os.path.join(CSRC, "lora_sgmv.hip"), os.path.join(CSRC, "lora_host.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    return "hipcc"
+
+
+def command(out: str = LIB):
+    # packed fp32 VALU instructions are disabled for every kernel
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Wall", "-I", INCLUDE, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            *SOURCES, "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

@@ -1,0 +1,315 @@
+// Host part of the library: status strings, argument checks, projection
+// family shapes, launch plans, adapter packing and batch routing.
+//
+// Packing follows the load pipeline of the MAX page ("MAX 的
+// max.pipelines.lora 模块解析", LoRAModel 加载时的处理管线): validate, pre-scale
+// B, zero-pad to max_lora_rank, fuse q/k/v, cast.  Scaling follows the vLLM
+// page ("vLLM LoRA 实现深度解析", §1: alpha/r, rsLoRA alpha/sqrt(r), folded into
+// B).  Routing follows the LoRAManagerV3 API page (sort_lora_batch,
+// get_lora_graph_inputs).
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "lora_internal.h"
+
+namespace lora {
+
+lora_status_t check_dims(const lora_dims_t* d)
+{
+    if (!d)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (d->hidden <= 0 || d->n_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 ||
+        d->max_lora_rank <= 0 || d->max_num_loras <= 0)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (d->dtype != LORA_DTYPE_F32 && d->dtype != LORA_DTYPE_BF16)
+        return LORA_ERR_INVALID_ARGUMENT;
+    const int64_t nq = (int64_t)d->n_heads * d->head_dim;
+    const int64_t nkv = (int64_t)d->n_kv_heads * d->head_dim;
+    if (nq > (1 << 24) || nkv > (1 << 24) || d->hidden > (1 << 24))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (d->hidden % 8 || nq % 8 || nkv % 8)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (d->max_lora_rank % 8 || d->max_lora_rank > kMaxRank)
+        return LORA_ERR_INVALID_ARGUMENT;
+    return LORA_OK;
+}
+
+lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs)
+{
+    lora_status_t st = check_dims(d);
+    if (st != LORA_OK)
+        return st;
+    const int nq = d->n_heads * d->head_dim;
+    const int nkv = d->n_kv_heads * d->head_dim;
+    FamilyShape f;
+    memset(&f, 0, sizeof(f));
+    if (family == LORA_FAMILY_QKV) {
+        f.in_f = d->hidden;
+        f.n_s = 3;
+        f.widths[0] = nq;
+        f.widths[1] = nkv;
+        f.widths[2] = nkv;
+    } else if (family == LORA_FAMILY_O) {
+        f.in_f = nq;
+        f.n_s = 1;
+        f.widths[0] = d->hidden;
+    } else {
+        return LORA_ERR_INVALID_ARGUMENT;
+    }
+    f.offs[0] = 0;
+    for (int s = 0; s < f.n_s; ++s)
+        f.offs[s + 1] = f.offs[s] + f.widths[s];
+    f.out_f = f.offs[f.n_s];
+    f.R = d->max_lora_rank;
+    f.C = f.n_s * f.R;
+    f.L = d->max_num_loras;
+    f.elem = d->dtype == LORA_DTYPE_BF16 ? 2 : 4;
+    *fs = f;
+    return LORA_OK;
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static ShrinkPlan plan_from_tiles(const FamilyShape& fs, int n_tiles)
+{
+    ShrinkPlan p;
+    p.n_tiles = n_tiles;
+    p.nz = (fs.C + kShrinkCols - 1) / kShrinkCols;
+    p.cb = ((fs.C + p.nz - 1) / p.nz + 15) / 16 * 16;
+    const int grains = (fs.in_f + kKGrain - 1) / kKGrain;
+    const int blocks = std::max(1, n_tiles * p.nz);
+    int S = (kShrinkTargetBlocks + blocks - 1) / blocks;
+    S = std::min(std::max(S, 1), grains);
+    p.kc = (grains + S - 1) / S * kKGrain;
+    p.S = (fs.in_f + p.kc - 1) / p.kc;
+    if (p.S > 1) {
+        p.counter_bytes = align256((size_t)n_tiles * p.nz * sizeof(uint32_t));
+        p.partial_bytes = (size_t)n_tiles * p.S * kTileM * fs.C * sizeof(float);
+    } else {
+        p.counter_bytes = 0;
+        p.partial_bytes = 0;
+    }
+    return p;
+}
+
+ShrinkPlan plan_shrink(const FamilyShape& fs, int64_t end, int groups)
+{
+    int n_tiles = end > 0 ? (int)((end + kTileM - 1) / kTileM) + groups : 0;
+    return plan_from_tiles(fs, n_tiles);
+}
+
+size_t shrink_workspace_bound(const FamilyShape& fs, int64_t max_tokens)
+{
+    if (max_tokens <= 0)
+        return 0;
+    const int most = (int)((max_tokens + kTileM - 1) / kTileM) + fs.L;
+    size_t best = 0;
+    for (int t = 1; t <= most; ++t) {
+        ShrinkPlan p = plan_from_tiles(fs, t);
+        best = std::max(best, p.counter_bytes + p.partial_bytes);
+    }
+    return best;
+}
+
+// Round to nearest even bf16: add half an ulp (minus one when the kept part
+// is even) and truncate; NaN keeps its sign and becomes quiet.
+static inline uint16_t to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace lora
+
+using namespace lora;
+
+extern "C" {
+
+int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char* lora_status_string(lora_status_t s)
+{
+    switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARGUMENT: return "LORA_ERR_INVALID_ARGUMENT";
+    case LORA_ERR_INVALID_ADAPTER: return "LORA_ERR_INVALID_ADAPTER";
+    case LORA_ERR_SLOT_OUT_OF_RANGE: return "LORA_ERR_SLOT_OUT_OF_RANGE";
+    case LORA_ERR_CAPACITY: return "LORA_ERR_CAPACITY";
+    case LORA_ERR_DEVICE: return "LORA_ERR_DEVICE";
+    case LORA_ERR_UNSPECIFIED: return "LORA_ERR_UNSPECIFIED";
+    default: return "LORA_ERR_UNKNOWN";
+    }
+}
+
+lora_status_t lora_family_shape(const lora_dims_t* dims, int32_t family, int32_t* in_features,
+                                int32_t* n_slices, int32_t* slice_widths, int32_t* out_features)
+{
+    if (!in_features || !n_slices || !slice_widths || !out_features)
+        return LORA_ERR_INVALID_ARGUMENT;
+    FamilyShape fs;
+    lora_status_t st = family_shape(dims, family, &fs);
+    if (st != LORA_OK)
+        return st;
+    *in_features = fs.in_f;
+    *n_slices = fs.n_s;
+    for (int s = 0; s < 4; ++s)
+        slice_widths[s] = s < fs.n_s ? fs.widths[s] : 0;
+    *out_features = fs.out_f;
+    return LORA_OK;
+}
+
+lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lora_alpha,
+                                int32_t use_rslora, int32_t bias_none, uint32_t target_mask,
+                                const float* A_q, const float* B_q, const float* A_k,
+                                const float* B_k, const float* A_v, const float* B_v,
+                                const float* A_o, const float* B_o, void* A_qkv_out,
+                                void* B_qkv_out, void* A_o_out, void* B_o_out)
+{
+    lora_status_t st = check_dims(dims);
+    if (st != LORA_OK)
+        return st;
+    if (!A_qkv_out || !B_qkv_out || !A_o_out || !B_o_out)
+        return LORA_ERR_INVALID_ARGUMENT;
+    // validation (bias, rank range, target whitelist)
+    if (!bias_none || rank < 1 || rank > dims->max_lora_rank || (target_mask & ~0xFu))
+        return LORA_ERR_INVALID_ADAPTER;
+    if (!(lora_alpha == lora_alpha))
+        return LORA_ERR_INVALID_ARGUMENT;
+    const float* A_in[4] = {A_q, A_k, A_v, A_o};
+    const float* B_in[4] = {B_q, B_k, B_v, B_o};
+    for (int p = 0; p < 4; ++p)
+        if (((target_mask >> p) & 1u) && (!A_in[p] || !B_in[p]))
+            return LORA_ERR_INVALID_ARGUMENT;
+
+    const int64_t R = dims->max_lora_rank, r = rank;
+    const int64_t H = dims->hidden;
+    const int64_t nq = (int64_t)dims->n_heads * dims->head_dim;
+    const int64_t nkv = (int64_t)dims->n_kv_heads * dims->head_dim;
+    const int64_t in_p[4] = {H, H, H, nq};
+    const int64_t out_p[4] = {nq, nkv, nkv, H};
+    // A rows and B rows of each projection inside its packed tensor
+    const int64_t a_row0[4] = {0, R, 2 * R, 0};
+    const int64_t b_row0[4] = {0, nq, nq + nkv, 0};
+    void* A_dst[4] = {A_qkv_out, A_qkv_out, A_qkv_out, A_o_out};
+    void* B_dst[4] = {B_qkv_out, B_qkv_out, B_qkv_out, B_o_out};
+
+    const double scale = use_rslora ? (double)lora_alpha / sqrt((double)rank)
+                                    : (double)lora_alpha / (double)rank;
+    const float scale32 = (float)scale;
+    const bool bf16 = dims->dtype == LORA_DTYPE_BF16;
+
+    for (int p = 0; p < 4; ++p) {
+        const bool on = (target_mask >> p) & 1u;
+        // A block: rows [a_row0, a_row0 + R) of width in_p; rows >= rank are zero
+        for (int64_t i = 0; i < R; ++i) {
+            const int64_t row = a_row0[p] + i;
+            for (int64_t k = 0; k < in_p[p]; ++k) {
+                float v = (on && i < r) ? A_in[p][i * in_p[p] + k] : 0.0f;
+                if (bf16)
+                    ((uint16_t*)A_dst[p])[row * in_p[p] + k] = to_bf16(v);
+                else
+                    ((float*)A_dst[p])[row * in_p[p] + k] = v;
+            }
+        }
+        // B block: rows [b_row0, b_row0 + out_p) of width R; columns >= rank are zero
+        for (int64_t o = 0; o < out_p[p]; ++o) {
+            const int64_t row = b_row0[p] + o;
+            for (int64_t j = 0; j < R; ++j) {
+                float v = (on && j < r) ? B_in[p][o * r + j] * scale32 : 0.0f;
+                if (bf16)
+                    ((uint16_t*)B_dst[p])[row * R + j] = to_bf16(v);
+                else
+                    ((float*)B_dst[p])[row * R + j] = v;
+            }
+        }
+    }
+    return LORA_OK;
+}
+
+lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
+                                 const int64_t* row_offsets, int32_t max_num_loras,
+                                 int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,
+                                 int32_t* grouped_offsets, int32_t* num_groups, int64_t* end)
+{
+    if (num_requests < 0 || max_num_loras < 1 || !row_offsets || !sorted_row_offsets ||
+        !lora_ids || !grouped_offsets || !num_groups || !end)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (num_requests > 0 && (!request_slot || !perm))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (row_offsets[0] != 0)
+        return LORA_ERR_INVALID_ARGUMENT;
+    for (int32_t i = 0; i < num_requests; ++i) {
+        if (row_offsets[i + 1] < row_offsets[i])
+            return LORA_ERR_INVALID_ARGUMENT;
+        if (request_slot[i] < -1 || request_slot[i] >= max_num_loras)
+            return LORA_ERR_SLOT_OUT_OF_RANGE;
+    }
+
+    // adapter order by slot id; base (-1) after every adapter; stable
+    std::vector<int32_t> order((size_t)num_requests);
+    std::iota(order.begin(), order.end(), 0);
+    auto key = [&](int32_t i) -> int64_t {
+        return request_slot[i] < 0 ? (int64_t)max_num_loras : (int64_t)request_slot[i];
+    };
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return key(a) < key(b); });
+
+    // the routed token count must fit the int32 device offsets; checked before
+    // any output is written
+    int64_t lora_tokens = 0;
+    for (int32_t i = 0; i < num_requests; ++i) {
+        if (request_slot[order[i]] < 0)
+            break;
+        lora_tokens += row_offsets[order[i] + 1] - row_offsets[order[i]];
+    }
+    if (lora_tokens > 2147483647LL)
+        return LORA_ERR_INVALID_ARGUMENT;
+    int32_t G = 0;
+
+    sorted_row_offsets[0] = 0;
+    for (int32_t i = 0; i < num_requests; ++i) {
+        const int32_t a = order[i];
+        perm[i] = a;
+        sorted_row_offsets[i + 1] = sorted_row_offsets[i] + (row_offsets[a + 1] - row_offsets[a]);
+    }
+    // consecutive same-slot requests form a group; stop at the first base request
+    G = 0;
+    grouped_offsets[0] = 0;
+    for (int32_t i = 0; i < num_requests; ++i) {
+        const int32_t s = request_slot[order[i]];
+        if (s < 0)
+            break;
+        if (G == 0 || lora_ids[G - 1] != s) {
+            lora_ids[G] = s;
+            grouped_offsets[G] = (int32_t)sorted_row_offsets[i];
+            ++G;
+        }
+        grouped_offsets[G] = (int32_t)sorted_row_offsets[i + 1];
+    }
+    *num_groups = G;
+    *end = grouped_offsets[G];
+    return LORA_OK;
+}
+
+lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
+                                        int64_t max_tokens, size_t* bytes)
+{
+    if (!bytes || max_tokens < 0 || max_tokens > 2147483647LL)
+        return LORA_ERR_INVALID_ARGUMENT;
+    FamilyShape fs;
+    lora_status_t st = family_shape(dims, family, &fs);
+    if (st != LORA_OK)
+        return st;
+    *bytes = shrink_workspace_bound(fs, max_tokens);
+    return LORA_OK;
+}
+
+}  // extern "C"

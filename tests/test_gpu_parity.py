@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Workloads (synthetic, seeded; shapes of the pages' attention blocks):
+tiny (fp32), decode, prefill, mixed (bf16) at full size with every request
+checked; the 32-layer stack at full size with sampled rows of every layer.
+Every path (auto, VALU, MFMA) runs where it applies.  Edge cases: empty and
+base-only batches, the pages' base-only routing form, zero-length requests,
+ragged segment lengths around the tile size, zero B, rows at and past `end`,
+strided x/y, determinism and batch-composition invariance.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+import segmented_rank_gemv_amd as srg
+from lora_case import (TOL, U_TOL, GpuLayer, compare, dims_of, log, oracle_layer, pack_stacks,
+                       rel_err)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+PATHS = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA}
+_CACHE = {}
+
+
+def workload_case(name, layer=0):
+    key = (name, layer)
+    if key not in _CACHE:
+        w = synth.get_workload(name)
+        lengths, slots = synth.draw_requests(w)
+        ranks = synth.draw_ranks(w)
+        stacks = pack_stacks(w, layer, ranks)
+        acts = synth.draw_activations(w, layer, int(lengths.sum()))
+        ref = oracle_layer(w, stacks, lengths, slots, acts)
+        _CACHE[key] = (w, lengths, slots, stacks, acts, ref)
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
+def test_full_workload_parity(name, path):
+    w, lengths, slots, stacks, acts, ref = workload_case(name)
+    if path == "mfma" and w.dtype != "bf16":
+        pytest.skip("MFMA path is bf16 only")
+    log(f"[parity] workload={name} path={path} T={int(lengths.sum())}")
+    gl = GpuLayer(w, stacks, lengths, slots, acts)
+    gl.run(PATHS[path])
+    ey, eu = compare(w, gl, ref)
+    log(f"[parity] workload={name} path={path} y_rel={ey:.3e} u_rel={eu:.3e}")
+    assert ey <= TOL[w.dtype]
+    assert eu <= U_TOL[w.dtype]
+
+
+def test_stack_layers_sampled():
+    """Layers of the 32-layer stack at full size (first, last and some in
+    between); up to 8 sampled rows of every request checked against the oracle."""
+    w = synth.get_workload("stack")
+    lengths, slots = synth.draw_requests(w)
+    ranks = synth.draw_ranks(w)
+    T = int(lengths.sum())
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for layer in (0, 1, 11, 22, w.n_layers - 2, w.n_layers - 1):
+        stacks = pack_stacks(w, layer, ranks)
+        acts = synth.draw_activations(w, layer, T)
+        rows = {i: np.unique(np.concatenate([[0, lengths[i] - 1], rng.integers(0, lengths[i], 6)]))
+                for i in range(len(lengths))}
+        log(f"[stack] layer={layer}")
+        gl = GpuLayer(w, stacks, lengths, slots, acts)
+        gl.run(srg.PATH_AUTO)
+        ref = oracle_layer(w, stacks, lengths, slots, acts, token_rows=rows)
+        ey, eu = compare(w, gl, ref)
+        worst = max(worst, ey)
+        assert ey <= TOL[w.dtype], (layer, ey)
+        assert eu <= U_TOL[w.dtype], (layer, eu)
+    log(f"[stack] worst y_rel={worst:.3e}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+def small_bf16(L=4, R=16):
+    base = synth.get_workload("decode")
+    return synth.Workload(**{**base.__dict__, "name": "decode", "hidden": 512, "n_heads": 4,
+                             "n_kv_heads": 2, "head_dim": 128, "max_lora_rank": R,
+                             "max_num_loras": L})
+
+
+def run_custom(w, lengths, slots, path, ranks=None, targets="qkvo", zero_B=False, pad_rows=0,
+               pad_cols=0, layer=0):
+    lengths = np.asarray(lengths, np.int64)
+    slots = np.asarray(slots, np.int32)
+    ranks = np.full(w.max_num_loras, min(8, w.max_lora_rank), np.int32) if ranks is None else ranks
+    stacks = pack_stacks(w, layer, ranks, targets, zero_B)
+    acts = synth.draw_activations(w, layer, int(lengths.sum()))
+    gl = GpuLayer(w, stacks, lengths, slots, acts, pad_rows, pad_cols)
+    gl.run(path)
+    ref = oracle_layer(w, stacks, lengths, slots, acts)
+    return gl, ref, acts
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_ragged_segments_around_tile_size(path):
+    w = small_bf16(L=8)
+    lengths = [1, 15, 16, 17, 63, 64, 65, 127, 129, 3, 0, 200]
+    slots = [0, 1, 2, 3, 4, 5, 6, 7, 0, -1, 3, 1]
+    log(f"[ragged] path={path}")
+    gl, ref, _ = run_custom(w, lengths, slots, PATHS[path])
+    ey, eu = compare(w, gl, ref)
+    assert ey <= TOL["bf16"] and eu <= U_TOL["bf16"]
+
+
+@pytest.mark.parametrize("path", ["auto", "valu"])
+def test_tiny_fp32_odd_shapes(path):
+    w = synth.Workload(**{**synth.get_workload("tiny").__dict__, "hidden": 72, "n_heads": 3,
+                          "n_kv_heads": 1, "head_dim": 24, "max_lora_rank": 8, "max_num_loras": 3})
+    lengths = [2, 0, 70, 1, 9]
+    slots = [2, 0, 1, -1, 2]
+    gl, ref, _ = run_custom(w, lengths, slots, PATHS[path], ranks=np.array([3, 8, 5], np.int32))
+    ey, eu = compare(w, gl, ref)
+    assert ey <= TOL["f32"] and eu <= U_TOL["f32"]
+
+
+def test_empty_and_base_only_batches_are_noops():
+    w = small_bf16()
+    for lengths, slots in (([], []), ([3, 4], [-1, -1])):
+        gl, ref, acts = run_custom(w, lengths, slots, srg.PATH_AUTO)
+        assert gl.end == 0 and gl.G == 0
+        if len(lengths):
+            assert np.array_equal(gl.y_arrival("y_qkv"), acts["y_qkv"])
+            assert np.array_equal(gl.y_arrival("y_o"), acts["y_o"])
+
+
+def test_pages_base_only_form_leaves_y_unchanged():
+    """The base-only fallback routes every token to slot 0 holding an all-zero
+    adapter; y must come back bit-identical."""
+    w = small_bf16(L=2)
+    lengths = np.array([5, 70], np.int64)
+    stacks = pack_stacks(w, 0, np.full(2, 8, np.int32), targets="")
+    acts = synth.draw_activations(w, 0, 75)
+    gl = GpuLayer(w, stacks, lengths, np.array([0, 0], np.int32), acts)
+    gl.run(srg.PATH_AUTO)
+    assert gl.G == 1 and gl.end == 75
+    assert np.array_equal(gl.y_arrival("y_qkv"), acts["y_qkv"])
+    assert np.array_equal(gl.y_arrival("y_o"), acts["y_o"])
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_zero_B_gives_zero_delta(path):
+    w = small_bf16()
+    gl, ref, acts = run_custom(w, [3, 40, 90], [0, 1, 2], PATHS[path], zero_B=True)
+    assert np.array_equal(gl.y_arrival("y_qkv"), acts["y_qkv"])
+    assert np.array_equal(gl.y_arrival("y_o"), acts["y_o"])
+
+
+def test_rows_past_end_untouched_and_strided_buffers():
+    w = small_bf16()
+    gl, ref, acts = run_custom(w, [7, 33, 2, 5], [1, 0, -1, 1], srg.PATH_AUTO, pad_rows=9, pad_cols=8)
+    ey, _ = compare(w, gl, ref)
+    assert ey <= TOL["bf16"]
+    from lora_case import from_dev
+    for key in ("y_qkv_full", "y_o_full"):
+        full = from_dev(gl.dev[key])
+        assert np.all(full[gl.T:] [:, :-8] == 7.0)   # padded rows past the batch
+        assert np.all(full[:, -8:] == 0.0)            # padded columns
+
+
+def test_missing_projection_slice_unchanged():
+    w = small_bf16()
+    gl, ref, acts = run_custom(w, [10, 80], [0, 1], srg.PATH_AUTO, targets="qv")
+    y = gl.y_arrival("y_qkv")
+    k = slice(w.nq, w.nq + w.nkv)
+    assert np.array_equal(y[:, k], acts["y_qkv"][:, k])
+    assert np.array_equal(gl.y_arrival("y_o"), acts["y_o"])
+    ey, _ = compare(w, gl, ref)
+    assert ey <= TOL["bf16"]
+
+
+def test_padding_invariance_on_gpu():
+    """rank-8 adapters in R=8 and R=64 stacks give the same result within tolerance."""
+    res = []
+    for R in (8, 64):
+        w = small_bf16(L=2, R=R)
+        gl, ref, acts = run_custom(w, [20, 70], [0, 1], srg.PATH_AUTO, ranks=np.array([8, 8], np.int32))
+        res.append(gl.y_arrival("y_qkv"))
+    assert rel_err(res[1], res[0]) <= TOL["bf16"]
+
+
+def test_deterministic_and_batch_composition_invariant():
+    w = small_bf16()
+    lengths = [30, 1, 90, 4]
+    slots = [2, 0, 2, 1]
+    a, _, _ = run_custom(w, lengths, slots, srg.PATH_AUTO)
+    b, _, _ = run_custom(w, lengths, slots, srg.PATH_AUTO)
+    assert np.array_equal(a.y_arrival("y_qkv"), b.y_arrival("y_qkv"))
+    assert np.array_equal(a.y_arrival("y_o"), b.y_arrival("y_o"))
+    # request 2 alone vs inside the batch
+    alone, ref, _ = run_custom(w, [90], [2], srg.PATH_AUTO)
+    y_in_batch = a.y_arrival("y_qkv")[31:121]
+    assert rel_err(alone.y_arrival("y_qkv"), y_in_batch) <= TOL["bf16"]
+
+
+def test_host_side_argument_errors_launch_nothing():
+    w = small_bf16()
+    d = dims_of(w)
+    x = torch.zeros((4, w.hidden), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((w.max_num_loras, 3 * w.max_lora_rank, w.hidden), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    u = torch.zeros((4, 3 * w.max_lora_rank), dtype=torch.float32, device="cuda")
+    # misaligned x (one element in)
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x.view(-1)[1:1 + 3 * w.hidden].view(3, w.hidden), A,
+                             ids, offs, 1, 3, u)
+    assert e.value.code == 1
+    # workspace too small for a split-K launch
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, ids, offs, 1, 4, u,
+                             torch.zeros(4, dtype=torch.int32, device="cuda"))
+    assert e.value.code in (1, 4)
+    # more groups than slots
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, ids, offs, w.max_num_loras + 1, 4, u)
+    assert e.value.code == 1
+    # MFMA forced on fp32
+    d32 = srg.LoraDims(**{**d.__dict__, "dtype": "f32"})
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_expand(d32, srg.FAMILY_O, u, A, ids, offs, 1, 4, x, srg.PATH_MFMA)
+    assert e.value.code == 1
+    torch.cuda.synchronize()
