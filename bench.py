@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the segment-routed multi-adapter LoRA delta on one MI355X.
+
+A step is one batch through the whole hot path: host routing of the batch
+(lora_build_routing), upload of the routing arrays, then for every layer the
+fused-QKV delta (shrink + expand) and the o_proj delta (shrink + expand).
+Adapters are packed (lora_pack_adapter) once, at activation, before timing.
+
+Default workload: Llama-3-8B attention (hidden 4096, 32 heads, 8 kv heads,
+head_dim 128), 256 one-token decode requests, 8 adapter slots with ranks 8/16
+padded to 16, 25% base requests, bf16 data with fp32 accumulation, run over
+64 distinct layer replicas per step so that no layer's data is still in the
+256 MB last-level cache when it is read again.
+
+Output: one JSON line (rank 0).  `value` = LoRA-routed tokens x layers per
+second (tokens through one layer's q/k/v/o delta per second).
+
+Phases:
+  1. timed steps, the layer loop captured once in a HIP graph and replayed
+     (host routing + routing upload stay eager every step);
+  2. the same steps launched eagerly with HIP events around every kernel on
+     the launch stream: per-kernel average duration -> roofline of the
+     dominant kernel;
+  3. the CPU oracle on a bounded sample of the same workload (one core).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+REPLICAS = {"tiny": 1, "decode": 64, "prefill": 2, "mixed": 8, "stack": 32}
+KERNEL_SRC = os.path.join(ROOT, "segmented_rank_gemv_amd", "csrc", "lora_sgmv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode", choices=list(REPLICAS))
+    p.add_argument("--layers", type=int, default=0, help="override layer replicas per step")
+    p.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--api", default="delta", choices=["delta", "split"],
+                   help="delta: lora_sgmv_delta per family; split: lora_sgmv_shrink + lora_sgmv_expand")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import segmented_rank_gemv_amd as srg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    path = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA}[args.path]
+
+    w = synth.get_workload(args.workload)
+    n_layers = args.layers or REPLICAS[args.workload]
+    if args.workload == "stack" and not args.layers:
+        n_layers = w.n_layers
+    dims = srg.LoraDims(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank,
+                        w.max_num_loras, w.dtype)
+    lengths, slots = synth.draw_requests(w)
+    ranks = synth.draw_ranks(w)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(offsets[-1])
+    L, R = w.max_num_loras, w.max_lora_rank
+    bf16 = w.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    # routing once to lay the batch out in sorted order (the serving layer
+    # sorts its batch once; the timed steps still route on the host)
+    rt0 = srg.lora_build_routing(slots, offsets, L)
+    end, G = rt0["end"], rt0["num_groups"]
+    order = np.concatenate([np.arange(offsets[p], offsets[p + 1]) for p in rt0["perm"]])
+    fam_shape = {f: srg.lora_family_shape(dims, f) for f in (srg.FAMILY_QKV, srg.FAMILY_O)}
+    log(f"workload={w.name} T={T} end={end} G={G} layers={n_layers}")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if bf16:
+            return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    # ---- activation: pack every slot of every layer, upload stacks and data
+    t_pack = 0.0
+    n_pack = 0
+    layers = []
+    for l in range(n_layers):
+        st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+        for s in range(L):
+            wts = synth.draw_adapter(w, l, s, int(ranks[s]))
+            t0 = time.perf_counter()
+            pk = srg.lora_pack_adapter(dims, int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo", wts)
+            t_pack += time.perf_counter() - t0
+            n_pack += 1
+            for k in st:
+                st[k].append(pk[k])
+        acts = synth.draw_activations(w, l, T)
+        layer = {k: to_dev(np.stack(v)) for k, v in st.items()}
+        for k in ("x_qkv", "y_qkv", "x_o", "y_o"):
+            layer[k] = to_dev(np.ascontiguousarray(acts[k][order]))
+        layers.append(layer)
+        if (l + 1) % 16 == 0:
+            log(f"  prepared {l + 1}/{n_layers} layers")
+    u = {f: torch.zeros((max(end, 1), fam_shape[f][1] * R), dtype=torch.float32, device=dev)
+         for f in fam_shape}
+    ws = {f: torch.zeros(max(srg.lora_sgmv_workspace_bytes(dims, f, max(end, 1)), 16) // 4 + 4,
+                         dtype=torch.int32, device=dev) for f in fam_shape}
+    ids_dev = torch.zeros(L, dtype=torch.int32, device=dev)
+    offs_dev = torch.zeros(L + 1, dtype=torch.int32, device=dev)
+    ids_pin = torch.zeros(L, dtype=torch.int32).pin_memory()
+    offs_pin = torch.zeros(L + 1, dtype=torch.int32).pin_memory()
+
+    def route_and_upload():
+        rt = srg.lora_build_routing(slots, offsets, L)
+        assert rt["end"] == end and rt["num_groups"] == G
+        ids_pin[:G].copy_(torch.from_numpy(rt["lora_ids"]))
+        offs_pin[:G + 1].copy_(torch.from_numpy(rt["grouped_offsets"]))
+        ids_dev.copy_(ids_pin, non_blocking=True)
+        offs_dev.copy_(offs_pin, non_blocking=True)
+
+    FAMS = ((srg.FAMILY_QKV, "qkv", "x_qkv", "y_qkv", "A_qkv", "B_qkv"),
+            (srg.FAMILY_O, "o", "x_o", "y_o", "A_o", "B_o"))
+    if args.api == "delta":
+        KINDS = ("delta_qkv", "delta_o")
+    else:
+        KINDS = ("shrink_qkv", "expand_qkv", "shrink_o", "expand_o")
+
+    def layer_pass(ly, events=None):
+        def rec(kind, i):
+            if events is not None:
+                events[kind][i].record()
+        for f, nm, xk, yk, ak, bk in FAMS:
+            if args.api == "delta":
+                rec("delta_" + nm, 0)
+                srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], ids_dev, offs_dev, G, end, ly[yk],
+                                    ws[f], path)
+                rec("delta_" + nm, 1)
+            else:
+                rec("shrink_" + nm, 0)
+                srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], ids_dev, offs_dev, G, end, u[f], ws[f], path)
+                rec("shrink_" + nm, 1)
+                rec("expand_" + nm, 0)
+                srg.lora_sgmv_expand(dims, f, u[f], ly[bk], ids_dev, offs_dev, G, end, ly[yk], path)
+                rec("expand_" + nm, 1)
+
+    def all_layers():
+        for ly in layers:
+            layer_pass(ly)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        route_and_upload()
+        all_layers()  # first eager pass (also loads the code objects)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            all_layers()
+        torch.cuda.synchronize()
+
+    def step():
+        route_and_upload()
+        if graph is not None:
+            graph.replay()
+        else:
+            all_layers()
+
+    # ---- phase 1: timed steps
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"phase 1: {ms_per_step:.4f} ms/step")
+
+    # ---- phase 2: eager steps with events around every call.  A bounded
+    # spin kernel (torch.cuda._sleep) runs first so that the host has queued
+    # the whole step before the GPU reaches it: the events then time the
+    # kernels back to back, not the host's launch rate.
+    ev_steps = max(1, min(args.steps, 50))
+    pairs = {k: [] for k in KINDS}
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            route_and_upload()
+            all_layers()
+        torch.cuda.synchronize()
+        # host time to enqueue one instrumented step, and the spin rate
+        t0 = time.perf_counter()
+        route_and_upload()
+        for ly in layers:
+            layer_pass(ly, {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                            for k in KINDS})
+        enqueue_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        s_per_cycle = max(e0.elapsed_time(e1) * 1e-3 / 1e6, 1e-12)
+        spin = int(min(2.0 * enqueue_s / s_per_cycle, 2e10))
+        for _ in range(ev_steps):
+            torch.cuda._sleep(spin)
+            route_and_upload()
+            for ly in layers:
+                ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for k in KINDS}
+                layer_pass(ly, ev)
+                for k in KINDS:
+                    pairs[k].append(ev[k])
+            torch.cuda.synchronize()
+    avg_us = {k: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in pairs[k]])) for k in KINDS}
+    log("phase 2: " + " ".join(f"{k}={v:.2f}us" for k, v in avg_us.items()))
+
+    # algorithmic bytes per call (u, the rank-space intermediate, counted for
+    # the split calls that move it through memory; not for the delta call)
+    b = 2 if bf16 else 4
+    kbytes, kflops = {}, {}
+    for f, nm, *_ in FAMS:
+        fin, n_s, widths, fout = fam_shape[f]
+        C = n_s * R
+        x_b, a_b = end * fin * b, G * C * fin * b
+        b_b, y_b = G * fout * R * b, 2 * end * fout * b
+        u_b = end * C * 4
+        kbytes["shrink_" + nm] = x_b + a_b + u_b
+        kbytes["expand_" + nm] = u_b + b_b + y_b
+        kbytes["delta_" + nm] = x_b + a_b + b_b + y_b
+        kflops["shrink_" + nm] = 2 * end * C * fin
+        kflops["expand_" + nm] = 2 * end * fout * R
+        kflops["delta_" + nm] = kflops["shrink_" + nm] + kflops["expand_" + nm]
+    fam_bytes = sum(kbytes["delta_" + nm] for _, nm, *_ in FAMS)
+    dominant = max(KINDS, key=lambda k: avg_us[k])
+    achieved = kbytes[dominant] / (avg_us[dominant] * 1e-6) / 1e9
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        key = f"{w.name}:{dominant}"
+        if tr.get("kernel_sha") == kernel_sha() and key in tr.get("kernels", {}):
+            traffic = tr["kernels"][key]["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    value = end * n_layers / (ms_per_step * 1e-3)
+    e2e_gbs = fam_bytes * n_layers / (ms_per_step * 1e-3) / 1e9
+
+    # ---- phase 3: CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        tokens_done = 0
+        t_cpu = 0.0
+        sample_layers = 0
+        for l in range(n_layers):
+            st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+            for s in range(L):
+                pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
+                                         int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
+                                         synth.draw_adapter(w, l, s, int(ranks[s])))
+                for k in st:
+                    st[k].append(pk[k])
+            st = {k: np.stack(v) for k, v in st.items()}
+            acts = synth.draw_activations(w, l, T)
+            lora_req = [i for i in range(len(slots)) if slots[i] >= 0]
+            # bound the work per layer for the long workloads
+            budget = max(1, int(2e8 // (fam_shape[0][0] * fam_shape[0][1] * R + fam_shape[0][3] * R)))
+            rows = {}
+            left = budget
+            for i in lora_req:
+                n = int(lengths[i])
+                rows[i] = np.arange(min(n, max(left, 0)))
+                left -= len(rows[i])
+            reqs = [i for i in lora_req if len(rows[i])]
+            t0 = time.perf_counter()
+            oracle.reference_family(acts["x_qkv"], acts["y_qkv"], offsets, slots, st["A_qkv"], st["B_qkv"],
+                                    [w.nq, w.nkv, w.nkv], R, w.dtype, reqs, rows)
+            oracle.reference_family(acts["x_o"], acts["y_o"], offsets, slots, st["A_o"], st["B_o"],
+                                    [w.hidden], R, w.dtype, reqs, rows)
+            t_cpu += time.perf_counter() - t0
+            tokens_done += sum(len(rows[i]) for i in reqs)
+            sample_layers += 1
+            if t_cpu >= args.cpu_seconds:
+                break
+        cpu = {"value": tokens_done / t_cpu, "unit": "LoRA tokens x layers / s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{tokens_done} LoRA-routed token rows over {sample_layers} layer(s) of the same "
+                         f"workload (q/k/v/o delta, fp64, single thread), {t_cpu:.1f} s"}
+        log(f"phase 3: oracle {cpu['value']:.1f} tokens x layers/s")
+
+    out = {
+        "metric": "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), Llama-8B QKV shape",
+        "value": value,
+        "unit": "LoRA tokens x layers / s (q/k/v/o delta)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded; adapters, activations and routing drawn per layer)",
+        "config": {"workload": w.name, "hidden": w.hidden, "n_heads": w.n_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "requests": int(len(slots)),
+                   "tokens": T, "lora_tokens": end, "groups": G, "max_num_loras": L,
+                   "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,
+                   "api": args.api,
+                   "hip_graph": graph is not None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
+                     "algorithmic_bytes_per_launch": kbytes[dominant],
+                     "avg_launch_us": avg_us[dominant]},
+        "calls": {k: {"avg_us": avg_us[k], "bytes": kbytes[k], "flops": kflops[k],
+                      "GBps": kbytes[k] / (avg_us[k] * 1e-6) / 1e9} for k in KINDS},
+        "end_to_end_GBps": e2e_gbs,
+        "pack_ms_per_adapter_layer": 1e3 * t_pack / max(n_pack, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,7 +81,7 @@ enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2 };
  * correspond to LoRAConfig.max_lora_rank / max_num_loras ([MAX-lora] LoRAConfig
  * table; page defaults 16 and 1).  Constraints checked by every call:
  * all fields > 0; hidden, n_heads*head_dim and n_kv_heads*head_dim multiples
- * of 8; max_lora_rank a multiple of 8 and <= 512; dtype one of LORA_DTYPE_*. */
+ * of 8 and at most 2^20; max_lora_rank a multiple of 8 and <= 128; dtype one of LORA_DTYPE_*. */
 typedef struct lora_dims {
     int32_t hidden;
     int32_t n_heads;
@@ -164,10 +164,11 @@ lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_sl
                                  int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,
                                  int32_t* grouped_offsets, int32_t* num_groups, int64_t* end);
 
-/* Workspace bytes lora_sgmv_shrink needs for a family, for any batch with at
- * most max_tokens LoRA-routed tokens and at most dims->max_num_loras groups.
- * The workspace must be zero-filled before its first use; every completed
- * shrink leaves its counter area zero again, so it can be reused as is. */
+/* Workspace bytes that lora_sgmv_shrink and lora_sgmv_delta need for a
+ * family, for any batch with at most max_tokens LoRA-routed tokens.  The
+ * workspace holds fp32 partial sums of u (one slab per K split of the shrink);
+ * its contents on entry do not matter and it needs no initialisation.
+ * Errors: LORA_ERR_INVALID_ARGUMENT for bad dims, family or max_tokens. */
 lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
                                         int64_t max_tokens, size_t* bytes);
 
@@ -186,11 +187,13 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
  * lora_ids, grouped_offsets: device int32 arrays of num_groups and
  *          num_groups+1 entries as produced by lora_build_routing.
  * u        fp32 [end][n_slices*R] (device).
- * workspace: device, >= lora_sgmv_workspace_bytes(dims, family, end), zero-filled
- *          before first use; NULL allowed when the call needs none.
+ * workspace: device scratch, >= lora_sgmv_workspace_bytes(dims, family, end)
+ *          bytes (NULL allowed when that is 0); used when K is split over
+ *          several workgroups, whose partial sums are then added in a fixed
+ *          order (results are deterministic).
  * path     LORA_PATH_*.
  * Alignment: x, A_stack, u and workspace 16-byte aligned; ldx*element size a
- * multiple of 16.  Malformed device routing cannot make the kernel access
+ * multiple of 16 and at most 2^24 bytes.  Malformed device routing cannot make the kernel access
  * memory outside [0, end) rows or the stacks (indices are clamped and bad
  * slot ids skipped), but the result is then unspecified.
  */
@@ -213,13 +216,35 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
  * u        fp32 [end][n_slices*R] (device), as lora_sgmv_shrink wrote it.
  * B_stack  [L][out_features][R] in dims->dtype.
  * y        [>= end rows][out_features] in dims->dtype, row stride ldy, updated in place.
- * Alignment: u, B_stack and y 16-byte aligned; ldy*element size a multiple of 16.
+ * Alignment: u, B_stack and y 16-byte aligned; ldy*element size a multiple of 16
+ * and at most 2^24 bytes.
  * u must not alias y.
  */
 lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
                                const void* B_stack, const int32_t* lora_ids,
                                const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
                                void* y, int64_t ldy, int32_t path, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lora_sgmv_delta — device, asynchronous on `stream`.
+ *
+ * The whole delta of one family in one call: the shrink followed by the
+ * boundary-aware expand ([vLLM] §6 lora_shrink then lora_expand; [MAX-V3]
+ * get_lora_graph_inputs for the routing and `end`), with the rank-space
+ * intermediate kept in `workspace` as fp32 partial sums that the expand adds
+ * in a fixed order:
+ *   y[t][off_s + o] = round(y[t][off_s + o]
+ *                     + sum_j B[slot][off_s + o][j] * sum_k A[slot][s*R + j][k] * x[t][k])
+ * for t < end, fp32 accumulation, one rounding to dims->dtype.  Rows >= end
+ * are neither read nor written.  Arguments as for lora_sgmv_shrink and
+ * lora_sgmv_expand; workspace >= lora_sgmv_workspace_bytes(dims, family, end)
+ * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
+ */
+lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
+                              const void* A_stack, const void* B_stack, const int32_t* lora_ids,
+                              const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
+                              void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              int32_t path, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     lora_build_routing,
     lora_family_shape,
     lora_pack_adapter,
+    lora_sgmv_delta,
     lora_sgmv_expand,
     lora_sgmv_shrink,
     lora_sgmv_workspace_bytes,

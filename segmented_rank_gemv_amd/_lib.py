@@ -90,6 +90,9 @@ def _load():
                                      i32, P]
     lib.lora_sgmv_expand.restype = i32
     lib.lora_sgmv_expand.argtypes = [D, i32, P, P, P, P, i32, i64, P, i64, i32, P]
+    lib.lora_sgmv_delta.restype = i32
+    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, P, i32, i64, P, i64, P, ctypes.c_size_t,
+                                    i32, P]
     _lib = lib
     return lib
 
@@ -242,6 +245,22 @@ def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, lora_ids, grouped_
                                      int(end), _dev_ptr(y, "y"), _row_stride(y, "y"), int(path),
                                      _stream_handle(stream)),
            "lora_sgmv_expand")
+
+
+def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, lora_ids, grouped_offsets,
+                    num_groups: int, end: int, y, workspace, path: int = PATH_AUTO,
+                    stream=None) -> None:
+    """y[:end] += per-segment B[slot] . (A[slot] . x), shrink and expand in one call."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dc = dims.c()
+    _check(_load().lora_sgmv_delta(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
+                                    _dev_ptr(A_stack, "A_stack"), _dev_ptr(B_stack, "B_stack"),
+                                    _dev_ptr(lora_ids, "lora_ids"),
+                                    _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
+                                    int(end), _dev_ptr(y, "y"), _row_stride(y, "y"),
+                                    _dev_ptr(workspace, "workspace"), ws_bytes, int(path),
+                                    _stream_handle(stream)),
+           "lora_sgmv_delta")
 
 
 def packed_to_torch(a: np.ndarray):

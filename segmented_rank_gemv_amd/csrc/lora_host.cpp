@@ -8,6 +8,7 @@
 // B).  Routing follows the LoRAManagerV3 API page (sort_lora_batch,
 // get_lora_graph_inputs).
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -29,7 +30,7 @@ lora_status_t check_dims(const lora_dims_t* d)
         return LORA_ERR_INVALID_ARGUMENT;
     const int64_t nq = (int64_t)d->n_heads * d->head_dim;
     const int64_t nkv = (int64_t)d->n_kv_heads * d->head_dim;
-    if (nq > (1 << 24) || nkv > (1 << 24) || d->hidden > (1 << 24))
+    if (nq > kMaxWidth || nkv > kMaxWidth || d->hidden > kMaxWidth)
         return LORA_ERR_INVALID_ARGUMENT;
     if (d->hidden % 8 || nq % 8 || nkv % 8)
         return LORA_ERR_INVALID_ARGUMENT;
@@ -72,47 +73,74 @@ lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs
     return LORA_OK;
 }
 
-static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+static int shrink_target_blocks()
+{
+    const char* v = getenv("LORA_SGMV_SHRINK_BLOCKS");
+    const int t = v && *v ? atoi(v) : 0;
+    return t > 0 ? t : kShrinkTargetBlocks;
+}
 
-static ShrinkPlan plan_from_tiles(const FamilyShape& fs, int n_tiles)
+static ShrinkPlan plan_from_tiles(const FamilyShape& fs, int n_tiles, int64_t end)
 {
     ShrinkPlan p;
     p.n_tiles = n_tiles;
+    p.end = end;
     p.nz = (fs.C + kShrinkCols - 1) / kShrinkCols;
     p.cb = ((fs.C + p.nz - 1) / p.nz + 15) / 16 * 16;
     const int grains = (fs.in_f + kKGrain - 1) / kKGrain;
     const int blocks = std::max(1, n_tiles * p.nz);
-    int S = (kShrinkTargetBlocks + blocks - 1) / blocks;
+    const int target = shrink_target_blocks();
+    int S = (target + blocks - 1) / blocks;
     S = std::min(std::max(S, 1), grains);
     p.kc = (grains + S - 1) / S * kKGrain;
     p.S = (fs.in_f + p.kc - 1) / p.kc;
-    if (p.S > 1) {
-        p.counter_bytes = align256((size_t)n_tiles * p.nz * sizeof(uint32_t));
-        p.partial_bytes = (size_t)n_tiles * p.S * kTileM * fs.C * sizeof(float);
-    } else {
-        p.counter_bytes = 0;
-        p.partial_bytes = 0;
-    }
+    p.slab_bytes = (size_t)end * fs.C * sizeof(float);
     return p;
 }
 
 ShrinkPlan plan_shrink(const FamilyShape& fs, int64_t end, int groups)
 {
     int n_tiles = end > 0 ? (int)((end + kTileM - 1) / kTileM) + groups : 0;
-    return plan_from_tiles(fs, n_tiles);
+    return plan_from_tiles(fs, n_tiles, end);
 }
 
-size_t shrink_workspace_bound(const FamilyShape& fs, int64_t max_tokens)
+size_t shrink_workspace(const ShrinkPlan& p) { return p.S > 1 ? (size_t)p.S * p.slab_bytes : 0; }
+
+size_t delta_workspace(const ShrinkPlan& p) { return (size_t)p.S * p.slab_bytes; }
+
+size_t workspace_bound(const FamilyShape& fs, int64_t max_tokens)
 {
-    if (max_tokens <= 0)
-        return 0;
-    const int most = (int)((max_tokens + kTileM - 1) / kTileM) + fs.L;
+    // A batch of `end` tokens has at least ceil(end / kTileM) + 1 tiles, and S
+    // only grows as the tile count shrinks: bound S * end over tile counts k.
+    // Once S reaches 1 the bound grows with end alone, so the scan stops there
+    // and the largest batch closes it.
     size_t best = 0;
-    for (int t = 1; t <= most; ++t) {
-        ShrinkPlan p = plan_from_tiles(fs, t);
-        best = std::max(best, p.counter_bytes + p.partial_bytes);
+    const int64_t most = (max_tokens + kTileM - 1) / kTileM;
+    for (int64_t k = 1; k <= most; ++k) {
+        const int64_t e = std::min<int64_t>(k * kTileM, max_tokens);
+        ShrinkPlan p = plan_from_tiles(fs, (int)std::min<int64_t>(k + 1, 1 << 30), e);
+        best = std::max(best, delta_workspace(p));
+        if (p.S == 1)
+            break;
+    }
+    if (most > 0) {
+        ShrinkPlan p = plan_from_tiles(fs, (int)std::min<int64_t>(most + 1, 1 << 30), max_tokens);
+        best = std::max(best, delta_workspace(p));
     }
     return best;
+}
+
+int expand_tile(const FamilyShape& fs)
+{
+    int ft = kExpandCols;
+    for (;;) {
+        bool ok = true;
+        for (int s = 0; s < fs.n_s; ++s)
+            ok = ok && fs.widths[s] % ft == 0;
+        if (ok || ft == 8)
+            return ft;
+        ft /= 2;
+    }
 }
 
 // Round to nearest even bf16: add half an ulp (minus one when the kept part
@@ -308,7 +336,7 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
     lora_status_t st = family_shape(dims, family, &fs);
     if (st != LORA_OK)
         return st;
-    *bytes = shrink_workspace_bound(fs, max_tokens);
+    *bytes = workspace_bound(fs, max_tokens);
     return LORA_OK;
 }
 

@@ -16,12 +16,19 @@ constexpr int kTileM = 64;
 constexpr int kShrinkCols = 64;
 // Granularity of the shrink's K chunks (4 waves x 32-element MFMA steps).
 constexpr int kKGrain = 128;
-// Output features one expand workgroup covers.
-constexpr int kExpandCols = 256;
-// Workgroups a shrink launch aims for before it stops splitting K.
+// Largest output-feature tile of one expand workgroup; the launch uses the
+// largest power of two <= this that divides every slice width, so that a
+// tile never straddles two slices.
+constexpr int kExpandCols = 128;
+// Workgroups a shrink launch aims for before it stops splitting K
+// (LORA_SGMV_SHRINK_BLOCKS overrides it for tuning).
 constexpr int kShrinkTargetBlocks = 512;
-// Largest rank the kernels accept.
-constexpr int kMaxRank = 512;
+// Largest rank the kernels accept (bounds the expand's LDS u tile to 32 KB).
+constexpr int kMaxRank = 128;
+// Largest width (hidden, q, k/v) and largest row stride in bytes of x / y:
+// they keep every per-tile buffer resource of the kernels below 2^31 bytes.
+constexpr int kMaxWidth = 1 << 20;
+constexpr int64_t kMaxRowBytes = 1 << 24;
 
 struct FamilyShape {
     int in_f;        // contraction length of the shrink
@@ -38,19 +45,27 @@ struct FamilyShape {
 lora_status_t check_dims(const lora_dims_t* d);
 lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs);
 
+// Split-K plan of the shrink.  With S > 1 the shrink writes S partial slabs
+// [S][end][C] (fp32) that the expand (or a reduce kernel) sums in split order.
 struct ShrinkPlan {
-    int n_tiles;           // token-tile slots launched (upper bound on real tiles)
-    int nz;                // column groups
-    int cb;                // columns per group (multiple of 16, <= kShrinkCols)
-    int S;                 // K splits
-    int kc;                // K chunk length (multiple of kKGrain)
-    size_t counter_bytes;  // per-(tile, column group) arrival counters, 256-byte padded
-    size_t partial_bytes;  // fp32 partial tiles [n_tiles][S][kTileM][C]
+    int n_tiles;  // token-tile slots launched (upper bound on real tiles)
+    int nz;       // column groups
+    int cb;       // columns per group (multiple of 16, <= kShrinkCols)
+    int S;        // K splits
+    int kc;       // K chunk length (multiple of kKGrain)
+    int64_t end;  // routed tokens
+    size_t slab_bytes;  // end * C * 4
 };
 
 // Plan for a given number of routed tokens and groups.
 ShrinkPlan plan_shrink(const FamilyShape& fs, int64_t end, int groups);
-// Workspace bytes covering every plan with end <= max_tokens, groups <= L.
-size_t shrink_workspace_bound(const FamilyShape& fs, int64_t max_tokens);
+// Workspace of lora_sgmv_shrink (slabs only when S > 1).
+size_t shrink_workspace(const ShrinkPlan& p);
+// Workspace of lora_sgmv_delta (always the S slabs).
+size_t delta_workspace(const ShrinkPlan& p);
+// Workspace covering both calls for every batch with end <= max_tokens.
+size_t workspace_bound(const FamilyShape& fs, int64_t max_tokens);
+// Output-feature tile of the expand for this family.
+int expand_tile(const FamilyShape& fs);
 
 }  // namespace lora

@@ -121,13 +121,21 @@ class GpuLayer:
             C = self.shape[fam][1] * w.max_lora_rank
             self.u[fam] = torch.full((max(self.end, 1), C), float("nan"), dtype=torch.float32, device="cuda")
             nb = srg.lora_sgmv_workspace_bytes(self.dims, fam, max(self.end, 1))
-            self.ws[fam] = torch.zeros(max(nb, 16) // 4 + 4, dtype=torch.int32, device="cuda")
+            self.ws[fam] = torch.full((max(nb, 16) // 4 + 4,), -1, dtype=torch.int32, device="cuda")
 
-    def run(self, path: int = srg.PATH_AUTO, families=(srg.FAMILY_QKV, srg.FAMILY_O)):
+    def run(self, path: int = srg.PATH_AUTO, families=(srg.FAMILY_QKV, srg.FAMILY_O),
+            fused: bool = False):
+        """fused=False: lora_sgmv_shrink then lora_sgmv_expand (u checked);
+        fused=True: lora_sgmv_delta (u stays internal)."""
         for fam in families:
             xk, yk = ("x_qkv", "y_qkv") if fam == srg.FAMILY_QKV else ("x_o", "y_o")
             A = self.st["A_qkv" if fam == srg.FAMILY_QKV else "A_o"]
             B = self.st["B_qkv" if fam == srg.FAMILY_QKV else "B_o"]
+            if fused:
+                log(f"  launch delta family={fam} path={path} end={self.end} G={self.G}")
+                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, self.ids, self.goffs, self.G,
+                                    self.end, self.dev[yk], self.ws[fam], path)
+                continue
             log(f"  launch shrink+expand family={fam} path={path} end={self.end} G={self.G}")
             srg.lora_sgmv_shrink(self.dims, fam, self.dev[xk], A, self.ids, self.goffs, self.G,
                                  self.end, self.u[fam], self.ws[fam], path)

@@ -44,17 +44,23 @@ def workload_case(name, layer=0):
     return _CACHE[key]
 
 
+@pytest.mark.parametrize("api", ["split", "delta", "delta_reduce"])
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
-def test_full_workload_parity(name, path):
+def test_full_workload_parity(name, path, api, monkeypatch):
+    """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
+    lora_sgmv_delta; delta_reduce: lora_sgmv_delta with its slabs folded by
+    the reduce kernel before the expand."""
     w, lengths, slots, stacks, acts, ref = workload_case(name)
     if path == "mfma" and w.dtype != "bf16":
         pytest.skip("MFMA path is bf16 only")
-    log(f"[parity] workload={name} path={path} T={int(lengths.sum())}")
+    if api == "delta_reduce":
+        monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1")
+    log(f"[parity] workload={name} path={path} api={api} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(PATHS[path])
-    ey, eu = compare(w, gl, ref)
-    log(f"[parity] workload={name} path={path} y_rel={ey:.3e} u_rel={eu:.3e}")
+    gl.run(PATHS[path], fused=api != "split")
+    ey, eu = compare(w, gl, ref, check_u=api == "split")
+    log(f"[parity] workload={name} path={path} api={api} y_rel={ey:.3e} u_rel={eu:.3e}")
     assert ey <= TOL[w.dtype]
     assert eu <= U_TOL[w.dtype]
 
@@ -75,9 +81,9 @@ def test_stack_layers_sampled():
                 for i in range(len(lengths))}
         log(f"[stack] layer={layer}")
         gl = GpuLayer(w, stacks, lengths, slots, acts)
-        gl.run(srg.PATH_AUTO)
+        gl.run(srg.PATH_AUTO, fused=layer % 2 == 1)
         ref = oracle_layer(w, stacks, lengths, slots, acts, token_rows=rows)
-        ey, eu = compare(w, gl, ref)
+        ey, eu = compare(w, gl, ref, check_u=layer % 2 == 0)
         worst = max(worst, ey)
         assert ey <= TOL[w.dtype], (layer, ey)
         assert eu <= U_TOL[w.dtype], (layer, eu)
@@ -105,14 +111,18 @@ def run_custom(w, lengths, slots, path, ranks=None, targets="qkvo", zero_B=False
     return gl, ref, acts
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("path", list(PATHS))
-def test_ragged_segments_around_tile_size(path):
+def test_ragged_segments_around_tile_size(path, fused):
     w = small_bf16(L=8)
-    lengths = [1, 15, 16, 17, 63, 64, 65, 127, 129, 3, 0, 200]
-    slots = [0, 1, 2, 3, 4, 5, 6, 7, 0, -1, 3, 1]
-    log(f"[ragged] path={path}")
-    gl, ref, _ = run_custom(w, lengths, slots, PATHS[path])
-    ey, eu = compare(w, gl, ref)
+    lengths = np.array([1, 15, 16, 17, 63, 64, 65, 127, 129, 3, 0, 200], np.int64)
+    slots = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, -1, 3, 1], np.int32)
+    log(f"[ragged] path={path} fused={fused}")
+    stacks = pack_stacks(w, 0, np.full(w.max_num_loras, 8, np.int32))
+    acts = synth.draw_activations(w, 0, int(lengths.sum()))
+    gl = GpuLayer(w, stacks, lengths, slots, acts)
+    gl.run(PATHS[path], fused=fused)
+    ey, eu = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts), check_u=not fused)
     assert ey <= TOL["bf16"] and eu <= U_TOL["bf16"]
 
 
@@ -194,16 +204,22 @@ def test_padding_invariance_on_gpu():
 
 def test_deterministic_and_batch_composition_invariant():
     w = small_bf16()
-    lengths = [30, 1, 90, 4]
-    slots = [2, 0, 2, 1]
-    a, _, _ = run_custom(w, lengths, slots, srg.PATH_AUTO)
-    b, _, _ = run_custom(w, lengths, slots, srg.PATH_AUTO)
+    lengths = np.array([30, 1, 90, 4], np.int64)
+    slots = np.array([2, 0, 2, 1], np.int32)
+    stacks = pack_stacks(w, 0, np.full(w.max_num_loras, 8, np.int32))
+    acts = synth.draw_activations(w, 0, int(lengths.sum()))
+    a = GpuLayer(w, stacks, lengths, slots, acts)
+    a.run(srg.PATH_AUTO)
+    b = GpuLayer(w, stacks, lengths, slots, acts)
+    b.run(srg.PATH_AUTO)
     assert np.array_equal(a.y_arrival("y_qkv"), b.y_arrival("y_qkv"))
     assert np.array_equal(a.y_arrival("y_o"), b.y_arrival("y_o"))
-    # request 2 alone vs inside the batch
-    alone, ref, _ = run_custom(w, [90], [2], srg.PATH_AUTO)
-    y_in_batch = a.y_arrival("y_qkv")[31:121]
-    assert rel_err(alone.y_arrival("y_qkv"), y_in_batch) <= TOL["bf16"]
+    # request 2 (tokens 31..120) alone, with the same rows, vs inside the batch
+    alone_acts = {k: v[31:121] for k, v in acts.items()}
+    c = GpuLayer(w, stacks, np.array([90]), np.array([2], np.int32), alone_acts)
+    c.run(srg.PATH_AUTO)
+    for key in ("y_qkv", "y_o"):
+        assert rel_err(c.y_arrival(key), a.y_arrival(key)[31:121]) <= TOL["bf16"]
 
 
 def test_host_side_argument_errors_launch_nothing():

@@ -132,7 +132,7 @@ def test_pack_error_codes_match_oracle(kw, code):
 def test_pack_bad_dims_rejected():
     w = synth.get_workload("tiny")
     weights = synth.draw_adapter(w, 0, 0, 4)
-    for bad in (dict(hidden=0), dict(n_heads=3, head_dim=3), dict(max_lora_rank=12), dict(dtype="f32", max_lora_rank=1024)):
+    for bad in (dict(hidden=0), dict(n_heads=3, head_dim=3), dict(max_lora_rank=12), dict(dtype="f32", max_lora_rank=256)):
         d = srg.LoraDims(**{**dims_of(w).__dict__, **bad})
         with pytest.raises(srg.LoraError) as e:
             srg.lora_pack_adapter(d, 4, 8.0, False, True, "qkvo", weights)
