@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--api", default="delta", choices=["delta", "split"],
                    help="delta: lora_sgmv_delta per family; split: lora_sgmv_shrink + lora_sgmv_expand")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--device-routing", action="store_true",
+                   help="kernels read the routing from device memory only (no host copies)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true")
     return p.parse_args()
@@ -140,10 +142,17 @@ def main():
     offs_dev = torch.zeros(L + 1, dtype=torch.int32, device=dev)
     ids_pin = torch.zeros(L, dtype=torch.int32).pin_memory()
     offs_pin = torch.zeros(L + 1, dtype=torch.int32).pin_memory()
+    # the routing the kernels see: device arrays (refreshed every step) plus,
+    # unless --device-routing, host copies passed as launch arguments
+    routing = srg.LoraRouting(ids_dev, offs_dev, G, end,
+                              None if args.device_routing else rt0["lora_ids"],
+                              None if args.device_routing else rt0["grouped_offsets"])
 
     def route_and_upload():
         rt = srg.lora_build_routing(slots, offsets, L)
         assert rt["end"] == end and rt["num_groups"] == G
+        assert np.array_equal(rt["lora_ids"], rt0["lora_ids"])
+        assert np.array_equal(rt["grouped_offsets"], rt0["grouped_offsets"])
         ids_pin[:G].copy_(torch.from_numpy(rt["lora_ids"]))
         offs_pin[:G + 1].copy_(torch.from_numpy(rt["grouped_offsets"]))
         ids_dev.copy_(ids_pin, non_blocking=True)
@@ -163,15 +172,14 @@ def main():
         for f, nm, xk, yk, ak, bk in FAMS:
             if args.api == "delta":
                 rec("delta_" + nm, 0)
-                srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], ids_dev, offs_dev, G, end, ly[yk],
-                                    ws[f], path)
+                srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path)
                 rec("delta_" + nm, 1)
             else:
                 rec("shrink_" + nm, 0)
-                srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], ids_dev, offs_dev, G, end, u[f], ws[f], path)
+                srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], routing, u[f], ws[f], path)
                 rec("shrink_" + nm, 1)
                 rec("expand_" + nm, 0)
-                srg.lora_sgmv_expand(dims, f, u[f], ly[bk], ids_dev, offs_dev, G, end, ly[yk], path)
+                srg.lora_sgmv_expand(dims, f, u[f], ly[bk], routing, ly[yk], path)
                 rec("expand_" + nm, 1)
 
     def all_layers():
@@ -344,7 +352,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "requests": int(len(slots)),
                    "tokens": T, "lora_tokens": end, "groups": G, "max_num_loras": L,
                    "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,
-                   "api": args.api,
+                   "api": args.api, "routing": "device" if args.device_routing else "host+device",
                    "hip_graph": graph is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -73,8 +73,9 @@ enum { LORA_TARGET_Q = 1, LORA_TARGET_K = 2, LORA_TARGET_V = 4, LORA_TARGET_O = 
 
 /* Kernel path selection for the device calls.  AUTO picks per token tile:
  * wavefront-reduction VALU code for short (decode-shaped) tiles, MFMA for
- * longer bf16 tiles.  VALU / MFMA force one path (MFMA needs bf16, a rank that
- * is a multiple of 16 and slice widths that are multiples of 16). */
+ * longer bf16 tiles.  VALU / MFMA force one path (MFMA needs bf16; for the
+ * expand also a rank that is a multiple of 16 and at most 64 and slice widths
+ * that are multiples of 32). */
 enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2 };
 
 /* Model and LoRA capacity dimensions.  max_lora_rank (R) and max_num_loras (L)
@@ -173,10 +174,45 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
                                         int64_t max_tokens, size_t* bytes);
 
 /* ---------------------------------------------------------------------------
+ * The routing triple of one batch, as lora_build_routing produces it and as
+ * [MAX-V3] get_lora_graph_inputs() hands it to the kernels: lora_ids and
+ * grouped_offsets in device memory, `end` on the host.
+ *
+ * lora_ids         device int32[num_groups]: slot of each group.
+ * grouped_offsets  device int32[num_groups + 1]: token offsets of the groups
+ *                  in the sorted batch ([0] = 0, [num_groups] = end).
+ * num_groups       G, 0 <= G <= max_num_loras.
+ * end              LoRA-routed tokens, 0 <= end < 2^31.
+ * host_lora_ids, host_grouped_offsets
+ *                  optional host copies of the same two arrays (both or
+ *                  neither; NULL = none).  When given and G <=
+ *                  LORA_MAX_HOST_GROUPS, the device calls check them and pass
+ *                  them to the kernels as launch arguments, so no kernel reads
+ *                  the device arrays (which may then be NULL) before its first
+ *                  data load.  They are read at call time: launches recorded
+ *                  into a HIP graph keep the routing of the recording call.
+ * A base-only or empty batch (G = 0 or end = 0) makes every device call a
+ * no-op (the base-only routing of [MAX-lora] 运行时工作流与调度交互 — all tokens
+ * on slot 0 holding all-zero adapters — is also valid and leaves y as is).
+ * Malformed device arrays cannot make a kernel access rows outside [0, end)
+ * or memory outside the stacks (indices are clamped, bad slot ids skipped),
+ * but the results are then unspecified.
+ */
+#define LORA_MAX_HOST_GROUPS 64
+typedef struct lora_routing {
+    const int32_t* lora_ids;
+    const int32_t* grouped_offsets;
+    int32_t num_groups;
+    int64_t end;
+    const int32_t* host_lora_ids;
+    const int32_t* host_grouped_offsets;
+} lora_routing_t;
+
+/* ---------------------------------------------------------------------------
  * lora_sgmv_shrink — device, asynchronous on `stream`.
  *
  * [vLLM] §6 lora_shrink (A·x, hidden -> rank) over the segments of the
- * routing triple ([MAX-V3] get_lora_graph_inputs):
+ * routing triple:
  *   u[t][c] = sum_k A[lora_ids[g]][c][k] * x[t][k]
  *   for t in [grouped_offsets[g], grouped_offsets[g+1]), g < num_groups,
  *   c < n_slices*R, accumulated in fp32.
@@ -184,8 +220,7 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
  * x        [>= end rows][in_features] in dims->dtype, row stride ldx elements;
  *          rows >= end are not read.
  * A_stack  [L][n_slices*R][in_features] in dims->dtype (the family's packed stack).
- * lora_ids, grouped_offsets: device int32 arrays of num_groups and
- *          num_groups+1 entries as produced by lora_build_routing.
+ * routing  see lora_routing_t.
  * u        fp32 [end][n_slices*R] (device).
  * workspace: device scratch, >= lora_sgmv_workspace_bytes(dims, family, end)
  *          bytes (NULL allowed when that is 0); used when K is split over
@@ -193,15 +228,11 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
  *          order (results are deterministic).
  * path     LORA_PATH_*.
  * Alignment: x, A_stack, u and workspace 16-byte aligned; ldx*element size a
- * multiple of 16 and at most 2^24 bytes.  Malformed device routing cannot make the kernel access
- * memory outside [0, end) rows or the stacks (indices are clamped and bad
- * slot ids skipped), but the result is then unspecified.
+ * multiple of 16 and at most 2^24 bytes.
  */
 lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                               const void* A_stack, const int32_t* lora_ids,
-                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
-                               float* u, void* workspace, size_t workspace_bytes, int32_t path,
-                               void* stream);
+                               const void* A_stack, const lora_routing_t* routing, float* u,
+                               void* workspace, size_t workspace_bytes, int32_t path, void* stream);
 
 /* ---------------------------------------------------------------------------
  * lora_sgmv_expand — device, asynchronous on `stream`.
@@ -215,15 +246,14 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
  *
  * u        fp32 [end][n_slices*R] (device), as lora_sgmv_shrink wrote it.
  * B_stack  [L][out_features][R] in dims->dtype.
+ * routing  see lora_routing_t.
  * y        [>= end rows][out_features] in dims->dtype, row stride ldy, updated in place.
  * Alignment: u, B_stack and y 16-byte aligned; ldy*element size a multiple of 16
- * and at most 2^24 bytes.
- * u must not alias y.
+ * and at most 2^24 bytes.  u must not alias y.
  */
 lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
-                               const void* B_stack, const int32_t* lora_ids,
-                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
-                               void* y, int64_t ldy, int32_t path, void* stream);
+                               const void* B_stack, const lora_routing_t* routing, void* y,
+                               int64_t ldy, int32_t path, void* stream);
 
 /* ---------------------------------------------------------------------------
  * lora_sgmv_delta — device, asynchronous on `stream`.
@@ -241,8 +271,7 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
  */
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                              const void* A_stack, const void* B_stack, const int32_t* lora_ids,
-                              const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
+                              const void* A_stack, const void* B_stack, const lora_routing_t* routing,
                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                               int32_t path, void* stream);
 

@@ -17,7 +17,9 @@ from ._lib import (  # noqa: F401
     PATH_AUTO,
     PATH_MFMA,
     PATH_VALU,
+    MAX_HOST_GROUPS,
     LoraDims,
+    LoraRouting,
     LoraError,
     family_shape,
     library_path,

@@ -40,6 +40,59 @@ class _LoraDims(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class _LoraRouting(ctypes.Structure):
+    _fields_ = [("lora_ids", ctypes.c_void_p), ("grouped_offsets", ctypes.c_void_p),
+                ("num_groups", ctypes.c_int32), ("end", ctypes.c_int64),
+                ("host_lora_ids", ctypes.c_void_p), ("host_grouped_offsets", ctypes.c_void_p)]
+
+
+MAX_HOST_GROUPS = 64
+
+
+class LoraRouting:
+    """The routing triple of a batch for the device calls: lora_ids and
+    grouped_offsets as int32 GPU tensors, `end` and the group count on the
+    host, and (by default) host copies of the two arrays, which the library
+    passes to the kernels as launch arguments."""
+
+    def __init__(self, lora_ids, grouped_offsets, num_groups: int, end: int,
+                 host_lora_ids: Optional[np.ndarray] = None,
+                 host_grouped_offsets: Optional[np.ndarray] = None):
+        self.lora_ids = lora_ids
+        self.grouped_offsets = grouped_offsets
+        self.num_groups = int(num_groups)
+        self.end = int(end)
+        self.host_lora_ids = None if host_lora_ids is None else np.ascontiguousarray(host_lora_ids, np.int32)
+        self.host_grouped_offsets = (None if host_grouped_offsets is None
+                                     else np.ascontiguousarray(host_grouped_offsets, np.int32))
+
+    @classmethod
+    def from_host(cls, routing: Dict[str, object], device="cuda", host_copy: bool = True,
+                  device_arrays: bool = True):
+        """Upload a lora_build_routing result; keep host copies if host_copy."""
+        import torch
+        ids = np.ascontiguousarray(routing["lora_ids"], np.int32)
+        offs = np.ascontiguousarray(routing["grouped_offsets"], np.int32)
+        d_ids = d_offs = None
+        if device_arrays:
+            d_ids = torch.from_numpy(ids if ids.size else np.zeros(1, np.int32)).to(device)
+            d_offs = torch.from_numpy(offs).to(device)
+        return cls(d_ids, d_offs, routing["num_groups"], routing["end"],
+                   ids if host_copy else None, offs if host_copy else None)
+
+    def c(self) -> _LoraRouting:
+        r = _LoraRouting()
+        r.lora_ids = None if self.lora_ids is None else _dev_ptr(self.lora_ids, "lora_ids")
+        r.grouped_offsets = None if self.grouped_offsets is None else _dev_ptr(self.grouped_offsets,
+                                                                             "grouped_offsets")
+        r.num_groups = self.num_groups
+        r.end = self.end
+        r.host_lora_ids = None if self.host_lora_ids is None else self.host_lora_ids.ctypes.data
+        r.host_grouped_offsets = (None if self.host_grouped_offsets is None
+                                  else self.host_grouped_offsets.ctypes.data)
+        return r
+
+
 @dataclass(frozen=True)
 class LoraDims:
     """Model and LoRA capacity dimensions.  The defaults of max_lora_rank and
@@ -58,7 +111,9 @@ class LoraDims:
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    """The library this process loads: liblora_sgmv.so next to this file, or
+    the file LORA_SGMV_LIB names (an alternative build, for A/B tuning)."""
+    return os.environ.get("LORA_SGMV_LIB") or _LIB_PATH
 
 
 _lib = None
@@ -68,9 +123,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError(f"{_LIB_PATH} is not built; run segmented_rank_gemv_amd.build.build()")
-    lib = ctypes.CDLL(_LIB_PATH)
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run segmented_rank_gemv_amd.build.build()")
+    lib = ctypes.CDLL(path)
     P, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     D = ctypes.POINTER(_LoraDims)
     lib.lora_abi_version.restype = i32
@@ -85,14 +141,13 @@ def _load():
     lib.lora_build_routing.argtypes = [i32, P, P, i32, P, P, P, P, P, P]
     lib.lora_sgmv_workspace_bytes.restype = i32
     lib.lora_sgmv_workspace_bytes.argtypes = [D, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    RT = ctypes.POINTER(_LoraRouting)
     lib.lora_sgmv_shrink.restype = i32
-    lib.lora_sgmv_shrink.argtypes = [D, i32, P, i64, P, P, P, i32, i64, P, P, ctypes.c_size_t,
-                                     i32, P]
+    lib.lora_sgmv_shrink.argtypes = [D, i32, P, i64, P, RT, P, P, ctypes.c_size_t, i32, P]
     lib.lora_sgmv_expand.restype = i32
-    lib.lora_sgmv_expand.argtypes = [D, i32, P, P, P, P, i32, i64, P, i64, i32, P]
+    lib.lora_sgmv_expand.argtypes = [D, i32, P, P, RT, P, i64, i32, P]
     lib.lora_sgmv_delta.restype = i32
-    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, P, i32, i64, P, i64, P, ctypes.c_size_t,
-                                    i32, P]
+    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, RT, P, i64, P, ctypes.c_size_t, i32, P]
     _lib = lib
     return lib
 
@@ -221,43 +276,36 @@ def _row_stride(t, what: str) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.stride(0), t.shape[1]))
 
 
-def lora_sgmv_shrink(dims: LoraDims, family: int, x, A_stack, lora_ids, grouped_offsets,
-                     num_groups: int, end: int, u, workspace=None, path: int = PATH_AUTO,
-                     stream=None) -> None:
+def lora_sgmv_shrink(dims: LoraDims, family: int, x, A_stack, routing: LoraRouting, u,
+                     workspace=None, path: int = PATH_AUTO, stream=None) -> None:
     """u[:end] = per-segment A[slot] . x (fp32), asynchronously on the stream."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dc = dims.c()
+    dc, rc = dims.c(), routing.c()
     _check(_load().lora_sgmv_shrink(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
-                                     _dev_ptr(A_stack, "A_stack"), _dev_ptr(lora_ids, "lora_ids"),
-                                     _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
-                                     int(end), _dev_ptr(u, "u"), _dev_ptr(workspace, "workspace"),
-                                     ws_bytes, int(path), _stream_handle(stream)),
+                                     _dev_ptr(A_stack, "A_stack"), ctypes.byref(rc), _dev_ptr(u, "u"),
+                                     _dev_ptr(workspace, "workspace"), ws_bytes, int(path),
+                                     _stream_handle(stream)),
            "lora_sgmv_shrink")
 
 
-def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, lora_ids, grouped_offsets,
-                     num_groups: int, end: int, y, path: int = PATH_AUTO, stream=None) -> None:
+def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, routing: LoraRouting, y,
+                     path: int = PATH_AUTO, stream=None) -> None:
     """y[:end] += per-segment B[slot] . u, in place, asynchronously on the stream."""
-    dc = dims.c()
+    dc, rc = dims.c(), routing.c()
     _check(_load().lora_sgmv_expand(ctypes.byref(dc), family, _dev_ptr(u, "u"),
-                                     _dev_ptr(B_stack, "B_stack"), _dev_ptr(lora_ids, "lora_ids"),
-                                     _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
-                                     int(end), _dev_ptr(y, "y"), _row_stride(y, "y"), int(path),
-                                     _stream_handle(stream)),
+                                     _dev_ptr(B_stack, "B_stack"), ctypes.byref(rc), _dev_ptr(y, "y"),
+                                     _row_stride(y, "y"), int(path), _stream_handle(stream)),
            "lora_sgmv_expand")
 
 
-def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, lora_ids, grouped_offsets,
-                    num_groups: int, end: int, y, workspace, path: int = PATH_AUTO,
-                    stream=None) -> None:
+def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, routing: LoraRouting, y,
+                    workspace, path: int = PATH_AUTO, stream=None) -> None:
     """y[:end] += per-segment B[slot] . (A[slot] . x), shrink and expand in one call."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dc = dims.c()
+    dc, rc = dims.c(), routing.c()
     _check(_load().lora_sgmv_delta(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
                                     _dev_ptr(A_stack, "A_stack"), _dev_ptr(B_stack, "B_stack"),
-                                    _dev_ptr(lora_ids, "lora_ids"),
-                                    _dev_ptr(grouped_offsets, "grouped_offsets"), int(num_groups),
-                                    int(end), _dev_ptr(y, "y"), _row_stride(y, "y"),
+                                    ctypes.byref(rc), _dev_ptr(y, "y"), _row_stride(y, "y"),
                                     _dev_ptr(workspace, "workspace"), ws_bytes, int(path),
                                     _stream_handle(stream)),
            "lora_sgmv_delta")

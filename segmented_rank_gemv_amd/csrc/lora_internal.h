@@ -19,7 +19,7 @@ constexpr int kKGrain = 128;
 // Largest output-feature tile of one expand workgroup; the launch uses the
 // largest power of two <= this that divides every slice width, so that a
 // tile never straddles two slices.
-constexpr int kExpandCols = 128;
+constexpr int kExpandCols = 256;
 // Workgroups a shrink launch aims for before it stops splitting K
 // (LORA_SGMV_SHRINK_BLOCKS overrides it for tuning).
 constexpr int kShrinkTargetBlocks = 512;

@@ -33,13 +33,20 @@
 // results.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "lora_internal.h"
+
+#ifndef LORA_SHRINK_KC
+#define LORA_SHRINK_KC 128
+#endif
 
 namespace lora {
 namespace {
 
 constexpr int kThreads = 256;
+// K elements one MFMA-shrink workgroup stages per pass (row runs of 2 KC bytes)
+constexpr int kShrinkKC = LORA_SHRINK_KC;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -65,38 +72,48 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 // than 2^31 bytes and every masked offset is kOOB plus a small constant.
 constexpr uint32_t kOOB = 0x80000000u;
 
-struct Buf {
+// Cache policy bits of an access (kKeep: default; kStream: non-temporal).
+// Measured on MI355X, non-temporal x / y accesses slowed both kernels, so
+// every access uses kKeep.
+enum CachePolicy { kKeep = 0, kStream = 2 };
+
+template <int POL = kKeep>
+struct BufT {
     __amdgpu_buffer_rsrc_t r;
-    __device__ __forceinline__ Buf(const void* base, uint32_t bytes)
+    __device__ __forceinline__ BufT(const void* base, uint32_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000))
     {
     }
     __device__ __forceinline__ uint4 ld16(uint32_t off) const
     {
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL));
     }
     __device__ __forceinline__ uint2 ld8(uint32_t off) const
     {
-        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POL));
     }
     __device__ __forceinline__ void st8(uint32_t off, uint2 v) const
     {
         typedef unsigned int u32x2 __attribute__((__vector_size__(8)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, POL);
     }
     __device__ __forceinline__ void st16(uint32_t off, uint4 v) const
     {
         typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, POL);
     }
 };
+typedef BufT<kKeep> Buf;
+typedef BufT<kStream> StreamBuf;
 
 // 8 consecutive elements of T as fp32
 template <typename T> struct Vec8;
 template <> struct Vec8<uint16_t> {
     typedef uint4 Raw;
-    static __device__ __forceinline__ Raw load_raw(const Buf& b, uint32_t off) { return b.ld16(off); }
-    static __device__ __forceinline__ void store_buf(const Buf& b, uint32_t off, const float* f)
+    template <class B>
+    static __device__ __forceinline__ Raw load_raw(const B& b, uint32_t off) { return b.ld16(off); }
+    template <class B>
+    static __device__ __forceinline__ void store_buf(const B& b, uint32_t off, const float* f)
     {
         uint4 v;
         v.x = f2bf_pair(f[0], f[1]);
@@ -139,11 +156,13 @@ template <> struct Vec8<float> {
     struct Raw {
         uint4 a, b;
     };
-    static __device__ __forceinline__ Raw load_raw(const Buf& b, uint32_t off)
+    template <class B>
+    static __device__ __forceinline__ Raw load_raw(const B& b, uint32_t off)
     {
         return Raw{b.ld16(off), b.ld16(off + 16)};
     }
-    static __device__ __forceinline__ void store_buf(const Buf& b, uint32_t off, const float* f)
+    template <class B>
+    static __device__ __forceinline__ void store_buf(const B& b, uint32_t off, const float* f)
     {
         b.st16(off, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                                __float_as_uint(f[3])));
@@ -192,6 +211,18 @@ struct TileInfo {
     int slot;  // adapter slot of the group
     int t0;    // first token (sorted order)
     int n;     // tokens in the tile, 1..kTileM
+    int glen;  // tokens in the whole group (decides the kernel path)
+};
+
+// Routing as the kernels see it: the device arrays, or (kr != 0) a copy of
+// them carried in the kernel arguments.
+struct RouteArgs {
+    const int* ids;
+    const int* offs;
+    int G, end, L;
+    int kr;
+    int k_offs[LORA_MAX_HOST_GROUPS + 1];
+    int k_ids[LORA_MAX_HOST_GROUPS];
 };
 
 // Locate token tile `tile`: groups are cut into kTileM-token tiles in group
@@ -200,21 +231,22 @@ struct TileInfo {
 // group holding `tile`.  Offsets are clamped into [0, end] and made
 // non-decreasing per group, so malformed routing cannot move accesses outside
 // rows [0, end).  Returns false past the last tile or for a bad slot id.
-__device__ bool locate_tile(const int* __restrict__ offs, const int* __restrict__ ids, int G,
-                            int end, int L, int tile, TileInfo& ti)
+__device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
 {
     const int lane = threadIdx.x & 63;
     int base = 0;
-    for (int c0 = 0; c0 < G; c0 += 64) {
+    for (int c0 = 0; c0 < r.G; c0 += 64) {
         const int i = c0 + lane;
         int s = 0, e = 0;
-        if (i < G) {
-            s = min(max(offs[i], 0), end);
-            e = min(max(offs[i + 1], s), end);
+        if (i < r.G) {
+            const int o0 = r.kr ? r.k_offs[i] : r.offs[i];
+            const int o1 = r.kr ? r.k_offs[i + 1] : r.offs[i + 1];
+            s = min(max(o0, 0), r.end);
+            e = min(max(o1, s), r.end);
         }
         const int nt = (e - s + kTileM - 1) / kTileM;
         const int incl = wave_incl_scan(nt);
-        const unsigned long long hit = __ballot(i < G && base + incl > tile);
+        const unsigned long long hit = __ballot(i < r.G && base + incl > tile);
         if (hit) {
             const int src = __ffsll((long long)hit) - 1;
             const int gs = __shfl(s, src, 64), ge = __shfl(e, src, 64);
@@ -223,14 +255,14 @@ __device__ bool locate_tile(const int* __restrict__ offs, const int* __restrict_
             ti.g = __builtin_amdgcn_readfirstlane(c0 + src);
             ti.t0 = __builtin_amdgcn_readfirstlane(gs + (tile - first) * kTileM);
             ti.n = __builtin_amdgcn_readfirstlane(min(kTileM, ge - gs - (tile - first) * kTileM));
-            ti.slot = __builtin_amdgcn_readfirstlane(ids[ti.g]);
-            return ti.slot >= 0 && ti.slot < L;
+            ti.glen = __builtin_amdgcn_readfirstlane(ge - gs);
+            ti.slot = __builtin_amdgcn_readfirstlane(r.kr ? r.k_ids[ti.g] : r.ids[ti.g]);
+            return ti.slot >= 0 && ti.slot < r.L;
         }
         base += __shfl(incl, 63, 64);
     }
     return false;
 }
-
 
 // ---------------------------------------------------------------------------
 // shrink
@@ -241,11 +273,10 @@ struct ShrinkArgs {
     const void* A;  // [L][C][in_f]
     float* out;     // slab s at out + s * slab, each [end][C]; S == 1: u itself
     int64_t slab;
-    const int* ids;
-    const int* offs;
-    int in_f, C, L, G, end;
+    int in_f, C;
     int S, kc, nz, cb;
     int valu_max;  // tiles with at most this many tokens take the VALU path
+    RouteArgs r;
 };
 
 // VALU path (decode-shaped tiles, and every fp32 tile).  A wave is four
@@ -318,142 +349,170 @@ __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int
     }
 }
 
-template <int NB>
-struct ShrinkFrags {
-    uint4 x[4];
-    uint4 a[NB];
+// LDS footprint (bf16 elements) of the MFMA shrink: x chunk [kTileM][KC + 8]
+// and A chunk [NB * 16][KC + 8]; the 8-element pad per row shifts
+// consecutive rows by 4 banks, so the 16-row fragment reads do not conflict.
+template <int NB, int KC>
+struct ShrinkLds {
+    static constexpr int kLd = KC + 8;
+    static constexpr int kX = kTileM * kLd;
+    static constexpr int kElems = kX + NB * 16 * kLd;
 };
 
-// MFMA path (bf16): the 4 waves take interleaved 32-element K steps
-// (k0 + 32 w + 128 j); each wave computes every 16-token x 16-column block
-// of the tile with v_mfma_f32_16x16x32_bf16, x rows as the M operand and A
-// rows as the N operand, both loaded straight from memory as 16-byte runs.
-// Fragments of the next step are loaded before the current step's MFMAs so
-// that two steps of loads are in flight per wave.  Wave partials land in
-// red[w][token][column].
-template <int NB>
+// MFMA path (bf16).  The workgroup walks its K chunk in pieces of KC
+// elements.  All 256 threads load a piece of the x tile [64 x KC] and of the
+// A tile [NB*16 x KC] as coalesced 16-byte runs (whole rows of KC elements),
+// stage them in LDS, and while the MFMAs consume one piece from LDS the
+// loads of the next piece are in flight.  Wave w owns the 16-token block w;
+// each 32-element step is one v_mfma_f32_16x16x32_bf16 per 16-column block,
+// x rows as the M operand and A rows as the N operand.  The wave writes its
+// 16 x cw block of the result directly.
+template <int NB, int KC>
 __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int k1, int c0,
-                            int c1, float* red, int red_ld)
+                            int c1, float* dst, int64_t dst_ld, uint16_t* lds)
 {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    typedef ShrinkLds<NB, KC> Lay;
+    constexpr int PIECES = KC / 8;  // 16-byte pieces per row
+    constexpr int XR = kTileM * PIECES / kThreads;
+    constexpr int APieces = NB * 16 * PIECES;
+    constexpr int AR = (APieces + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, q = lane >> 4;
+    uint16_t* lx = lds;
+    uint16_t* la = lds + Lay::kX;
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x) + (size_t)ti.t0 * a.ldx;
     const uint16_t* Ab = reinterpret_cast<const uint16_t*>(a.A) + ((size_t)ti.slot * a.C + c0) * a.in_f;
-    const Buf xb(X, (uint32_t)(ti.n * a.ldx * 2));
-    const Buf ab(Ab, (uint32_t)((c1 - c0) * a.in_f * 2));
-    const int mbn = (ti.n + 15) >> 4;
+    const Buf xb(X, (uint32_t)(ti.n * a.ldx * 2));             // rows past the tile read as zero
+    const Buf ab(Ab, (uint32_t)((c1 - c0) * a.in_f * 2));      // columns past the group read as zero
+    const int nchunks = (k1 - k0 + KC - 1) / KC;
 
-    uint32_t xrow[4], arow[NB];
+    uint4 xs[XR], as[AR];
+    auto gload = [&](int ch) {
+        const int kb = k0 + ch * KC;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-        xrow[mb] = (uint32_t)((mb * 16 + l16) * a.ldx) * 2;  // rows >= n fall outside xb
+        for (int i = 0; i < XR; ++i) {
+            const int p = tid + kThreads * i, r = p / PIECES, k = kb + 8 * (p % PIECES);
+            xs[i] = xb.ld16(k < k1 ? (uint32_t)(r * a.ldx + k) * 2 : kOOB);
+        }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        arow[nb] = (uint32_t)((nb * 16 + l16) * a.in_f) * 2;  // columns >= c1 fall outside ab
-
-    f32x4_t acc[4][NB];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](int kk, ShrinkFrags<NB>& f) {
-        const bool kin = kk < k1;
-        const uint32_t kb = 2u * (uint32_t)kk;
-        // unconditional loads (rows past the tile read as zero) keep the
-        // loop branch-free, so the wait before each MFMA covers only the
-        // fragments it consumes
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-            f.x[mb] = xb.ld16(kin ? xrow[mb] + kb : kOOB);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            f.a[nb] = ab.ld16(kin ? arow[nb] + kb : kOOB);
+        for (int i = 0; i < AR; ++i) {
+            const int p = tid + kThreads * i, r = p / PIECES, k = kb + 8 * (p % PIECES);
+            as[i] = ab.ld16((p < APieces && k < k1) ? (uint32_t)(r * a.in_f + k) * 2 : kOOB);
+        }
     };
-    auto mma = [&](const ShrinkFrags<NB>& f) {
+    auto lstore = [&]() {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            if (mb < mbn) {
-                const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, f.x[mb]);
+        for (int i = 0; i < XR; ++i) {
+            const int p = tid + kThreads * i;
+            *reinterpret_cast<uint4*>(lx + (p / PIECES) * Lay::kLd + 8 * (p % PIECES)) = xs[i];
+        }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        xv, __builtin_bit_cast(bf16x8_t, f.a[nb]), acc[mb][nb], 0, 0, 0);
-            }
+        for (int i = 0; i < AR; ++i) {
+            const int p = tid + kThreads * i;
+            if (p < APieces)
+                *reinterpret_cast<uint4*>(la + (p / PIECES) * Lay::kLd + 8 * (p % PIECES)) = as[i];
         }
     };
 
-    const int kw = k0 + 32 * w;
-    const int steps = kw < k1 ? (k1 - kw + 127) / 128 : 0;
-    const int kl = kw + 8 * q;
-    // Two fragment sets in flight.  Loads past k1 (the tail of the last pair)
-    // read zeros through kOOB, so the loop has no branches around its loads
-    // and its MFMAs add nothing for them.
-    ShrinkFrags<NB> fa, fb;
-    load(kl, fa);
-    for (int j = 0; j < steps; j += 2) {
-        load(kl + 128 * (j + 1), fb);
-        mma(fa);
-        load(kl + 128 * (j + 2), fa);
-        mma(fb);
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bool active = 16 * w < ti.n;
+
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        if (ch + 1 < nchunks)
+            gload(ch + 1);
+        if (active) {
+#pragma unroll
+            for (int st = 0; st < KC / 32; ++st) {
+                const int kk = 32 * st + 8 * q;
+                const bf16x8_t xv =
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + (16 * w + l16) * Lay::kLd + kk));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const bf16x8_t av = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const uint4*>(la + (nb * 16 + l16) * Lay::kLd + kk));
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, av, acc[nb], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+        if (ch + 1 < nchunks) {
+            lstore();
+            __syncthreads();
+        }
     }
+    if (!active)
+        return;
     // D[i][j]: lane holds column j = lane%16 and rows 4*(lane/16) + r
-    float* my = red + (size_t)w * kTileM * red_ld;
+    const int cw = c1 - c0;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        if (mb < mbn) {
+    for (int nb = 0; nb < NB; ++nb) {
+        const int c = nb * 16 + l16;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    my[(mb * 16 + 4 * q + r) * red_ld + nb * 16 + l16] = acc[mb][nb][r];
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * q + r;
+            if (t < ti.n && c < cw)
+                dst[(size_t)t * dst_ld + c] = acc[nb][r];
         }
     }
 }
+
+// Kernel variants: kMixed picks the path per tile (VALU for groups of at most
+// valu_max tokens, MFMA otherwise); kMfmaOnly / kValuOnly compile one path
+// only, which keeps the register budget of that path alone.
+enum { kMixed = 0, kMfmaOnly = 1, kValuOnly = 2 };
 
 // One workgroup per (token tile, K split, column group).  With one split the
 // result is u itself; with S splits each workgroup writes its split's slab
 // and the sum over splits is taken later, in split order, by the expand or
 // by reduce_slabs — there is no cross-workgroup synchronisation.
-template <typename T, int NB>
+template <typename T, int NB, int MODE>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
 {
     constexpr int CB = NB * 16;
-    constexpr bool kMfma = sizeof(T) == 2;
-    __shared__ float red[(kMfma ? 4 : 1) * kTileM * CB];
+    constexpr int KC = kShrinkKC;
+    constexpr bool kHasValu = MODE != kValuOnly ? MODE == kMixed : true;
+    constexpr bool kHasMfma = MODE != kValuOnly;
+    constexpr int kLdsBytes = (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0) > (kHasValu ? kTileM * CB * 4 : 0)
+                                  ? (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0)
+                                  : (kHasValu ? kTileM * CB * 4 : 0);
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes > 0 ? kLdsBytes : 16];
 
     const int lin = blockIdx.x;
     const int z = lin % a.nz;
     const int s = (lin / a.nz) % a.S;
     const int tile = lin / (a.nz * a.S);
     TileInfo ti;
-    if (!locate_tile(a.offs, a.ids, a.G, a.end, a.L, tile, ti))
+    if (!locate_tile(a.r, tile, ti))
         return;
     const int k0 = s * a.kc, k1 = min(k0 + a.kc, a.in_f);
     const int c0 = z * a.cb, c1 = min(c0 + a.cb, a.C);
     const int cw = c1 - c0;
-
-    bool use_mfma = false;
-    if constexpr (kMfma) {
-        use_mfma = ti.n > a.valu_max;
-        if (use_mfma)
-            shrink_mfma<NB>(a, ti, k0, k1, c0, c1, red, CB);
-        else
-            shrink_valu<T>(a, ti, k0, k1, c0, c1, red, CB);
-    } else {
-        shrink_valu<T>(a, ti, k0, k1, c0, c1, red, CB);
-    }
-    __syncthreads();
-
     float* dst = a.out + (size_t)s * a.slab + (size_t)ti.t0 * a.C + c0;
-    for (int e = threadIdx.x; e < ti.n * cw; e += kThreads) {
-        const int i = e / cw, c = e - i * cw;
-        float v = red[i * CB + c];
-        if (kMfma && use_mfma)
-            v = ((v + red[1 * kTileM * CB + i * CB + c]) + red[2 * kTileM * CB + i * CB + c]) +
-                red[3 * kTileM * CB + i * CB + c];
-        dst[(size_t)i * a.C + c] = v;
+
+    if constexpr (MODE == kMfmaOnly) {
+        shrink_mfma<NB, KC>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
+        return;
+    }
+    if constexpr (MODE == kMixed) {
+        if (ti.glen > a.valu_max) {
+            shrink_mfma<NB, KC>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
+            return;
+        }
+    }
+    if constexpr (kHasValu) {
+        float* res = reinterpret_cast<float*>(smem);
+        shrink_valu<T>(a, ti, k0, k1, c0, c1, res, CB);
+        __syncthreads();
+        for (int e = threadIdx.x; e < ti.n * cw; e += kThreads) {
+            const int i = e / cw, c = e - i * cw;
+            dst[(size_t)i * a.C + c] = res[i * CB + c];
+        }
     }
 }
 
@@ -486,13 +545,12 @@ struct ExpandArgs {
     const void* B;  // [L][out_f][R]
     void* y;
     int64_t ldy;
-    const int* ids;
-    const int* offs;
-    int C, R, L, G, end, n_s, out_f;
+    int C, R, n_s, out_f;
     int soff[5];  // slice offsets, soff[n_s] = out_f
     int ft;       // feature tile (divides every slice width)
     int n_ftiles;
     int valu_max;  // tiles with at most this many tokens take the VALU path
+    RouteArgs r;
 };
 
 __device__ __forceinline__ int slice_of(const ExpandArgs& a, int f)
@@ -504,8 +562,6 @@ __device__ __forceinline__ int slice_of(const ExpandArgs& a, int f)
             s = i;
     return s;
 }
-
-constexpr int kDeltaPad = 4;  // floats of padding per row of the LDS delta tile
 
 // Sum the S slabs of u for the tile's tokens and one slice's R columns into
 // LDS us[n][R] (fp32).  With many items per workgroup each thread adds all S
@@ -568,159 +624,150 @@ __device__ __forceinline__ void stage_u(const ExpandArgs& a, const TileInfo& ti,
     }
 }
 
-// MFMA delta of the tile into LDS (bf16).  The tile's (16-token x 16-feature)
-// blocks are dealt to the 4 waves round-robin.  For each block one
-// v_mfma_f32_16x16x32_bf16 per 16 ranks computes B·u with K = 32 = 16 ranks
-// of the high bf16 half of u followed by the same 16 ranks of its low half
+// MFMA path (bf16).  Wave w owns tokens 16w .. 16w+15 of the tile and walks
+// the feature tile in pairs of 16-feature MFMA blocks.  For each 16 ranks one
+// v_mfma_f32_16x16x32_bf16 per block computes B·u with K = 32 = 16 ranks of
+// the high bf16 half of u followed by the same 16 ranks of its low half
 // (u = hi + lo to ~2^-17 relative), so u keeps fp32 precision while the
 // products run on the bf16 matrix cores.  B rows are the M operand
-// (features), u the N operand (tokens).  bfr holds the B fragments, loaded
-// before u was staged.
+// (features) and u the N operand (tokens).  The M rows of block h of pair p
+// are permuted to features 32p + 8(i/4) + 4h + i%4, so that lane (token j,
+// group q) holds features 32p + 8q .. 32p + 8q + 7 across the two
+// accumulators: y is the C operand, read and written as 16-byte runs in the
+// MFMA layout itself, and a wave covers 16 rows x 512 contiguous bytes.
+// y and (for NH <= 2) B fragments are loaded before u is staged.
 template <int NH>
-__device__ __forceinline__ void mfma_delta(const ExpandArgs& a, const TileInfo& ti,
-                                           const uint4 (&bfr)[8][NH], const float* us, float* dl,
-                                           int dl_ld)
+__device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
+                                            const Buf& yb, int ucol0, float* us, float4* part)
 {
+    constexpr int kMaxPairs = kExpandCols / 32;
+    constexpr bool kPrefetchB = NH == 1;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, q = lane >> 4;
-    const int nfb = a.ft >> 4;
-    const int nblk = ((ti.n + 15) >> 4) * nfb;
-    int cur_tb = -1;
+    const int np = a.ft >> 5;
+    const int t = 16 * w + l16;
+    const bool tok = t < ti.n;
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0
+    const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * a.R;
+
+    uint4 yraw[kMaxPairs];
+#pragma unroll
+    for (int p = 0; p < kMaxPairs; ++p)
+        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
+    uint4 bfr[kPrefetchB ? kMaxPairs : 1][2][NH];
+    if constexpr (kPrefetchB) {
+#pragma unroll
+        for (int p = 0; p < kMaxPairs; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kh = 0; kh < NH; ++kh)
+                    bfr[p][h][kh] = ld16(Bb + (size_t)(min(p, np - 1) * 32 + mrow + 4 * h) * a.R + 16 * kh +
+                                         8 * (q & 1));
+    }
+
+    stage_u(a, ti, ucol0, us, part);
+    __syncthreads();
+    if (16 * w >= ti.n)
+        return;
+
+    // u fragments: lanes q<2 carry hi(u[t][16kh+8q..]), lanes q>=2 lo(u[t][16kh+8(q-2)..])
     bf16x8_t uf[NH];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int b = w + 4 * i;
-        if (b < nblk) {
-            const int tb = b / nfb, fb = b - tb * nfb;
-            const int t = tb * 16 + l16;
-            if (tb != cur_tb) {
-                cur_tb = tb;
-                // lanes q<2 carry hi(u[t][16h+8q..]), lanes q>=2 lo(u[t][16h+8(q-2)..])
+    for (int kh = 0; kh < NH; ++kh) {
+        const float* up = us + min(t, ti.n - 1) * a.R + 16 * kh + 8 * (q & 1);
+        uint32_t pk[4];
 #pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    float v[8];
-                    const float* up = us + min(t, ti.n - 1) * a.R + 16 * h + 8 * (q & 1);
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = up[2 * e], v1 = up[2 * e + 1];
+            uint32_t hi = f2bf_pair(v0, v1);
+            if (q >= 2)
+                hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+            pk[e] = hi;
+        }
+        uf[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[e] = up[e];
-                    uint32_t pk[4];
+    for (int p = 0; p < kMaxPairs; ++p) {
+        if (p < np) {
+            const uint4 yv = yraw[p];
+            f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
+            f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint32_t hi = f2bf_pair(v[2 * e], v[2 * e + 1]);
-                        if (q >= 2)
-                            hi = f2bf_pair(v[2 * e] - bf2f(hi & 0xFFFFu), v[2 * e + 1] - bf2f(hi >> 16));
-                        pk[e] = hi;
-                    }
-                    uf[h] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            for (int kh = 0; kh < NH; ++kh) {
+                uint4 b0, b1;
+                if constexpr (kPrefetchB) {
+                    b0 = bfr[p][0][kh];
+                    b1 = bfr[p][1][kh];
+                } else {
+                    const uint16_t* bp = Bb + (size_t)(p * 32 + mrow) * a.R + 16 * kh + 8 * (q & 1);
+                    b0 = ld16(bp);
+                    b1 = ld16(bp + 4 * a.R);
                 }
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[kh], acc0,
+                                                              0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[kh], acc1,
+                                                              0, 0, 0);
             }
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int h = 0; h < NH; ++h)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[i][h]), uf[h],
-                                                             acc, 0, 0, 0);
-            // D[i][j]: lane holds token j = lane%16, features 4*(lane/16) + r
-            *reinterpret_cast<f32x4_t*>(dl + t * dl_ld + fb * 16 + 4 * q) = acc;
+            uint4 o;
+            o.x = f2bf_pair(acc0[0], acc0[1]);
+            o.y = f2bf_pair(acc0[2], acc0[3]);
+            o.z = f2bf_pair(acc1[0], acc1[1]);
+            o.w = f2bf_pair(acc1[2], acc1[3]);
+            yb.st16(tok ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
         }
     }
 }
 
-// One workgroup per (token tile, feature tile).  Thread (rr, fl) owns
+// VALU path (decode-shaped tiles, and every fp32 tile).  Thread (rr, fl) owns
 // features f0 + 8 fl .. +8 of rows rr, rr + RP, ... (RP = rows per pass), so
-// every y access is a 16-byte run and a wave covers whole row segments.  The
-// y rows are loaded first, then u is staged; the delta comes from MFMA (long
-// bf16 tiles, through an LDS tile) or from VALU FMAs in registers (short
-// tiles and fp32); y + delta is rounded once and stored.
-// NH = R / 16 when the MFMA path may run (bf16, R <= 64, slice widths multiple
-// of 16); NH = 0 builds the VALU path alone.
-template <typename T, int NH>
-__global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
+// every y access is a 16-byte run and a wave covers whole row segments.  Row
+// passes go two at a time; the first two are loaded before u is staged.  B is
+// read 8 ranks at a time and reused for both rows.
+template <typename T>
+__device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo& ti, int f0,
+                                            const Buf& yb, int ucol0, float* us, float4* part)
 {
     constexpr int E = sizeof(T);
-    constexpr int kRows = 4;  // row passes per thread (feature tile <= 128)
-    extern __shared__ float smem[];
-    float* us = smem;                                        // [kTileM][R]
-    float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads] float4
-    float* dl = reinterpret_cast<float*>(part + kThreads);        // [kTileM][ft + pad]
-    const int dl_ld = a.ft + kDeltaPad;
-
-    const int lin = blockIdx.x;
-    const int ftile = lin % a.n_ftiles;
-    const int tile = lin / a.n_ftiles;
-    TileInfo ti;
-    if (!locate_tile(a.offs, a.ids, a.G, a.end, a.L, tile, ti))
-        return;
-    const int f0 = ftile * a.ft;
     const int fgroups = a.ft >> 3;
     const int rp = kThreads / fgroups;
     const int fl = threadIdx.x % fgroups, rr = threadIdx.x / fgroups;
     const int f = f0 + 8 * fl;
-    const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
+    const int npass = (ti.n + rp - 1) / rp;
 
-    typename Vec8<T>::Raw yraw[kRows];
+    typename Vec8<T>::Raw yraw[2];
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
+    for (int i = 0; i < 2; ++i) {
         const int row = rr + i * rp;
         yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(row * a.ldy + f) * E : kOOB);
     }
+    stage_u(a, ti, ucol0, us, part);
+    __syncthreads();
 
-    float delta[kRows][8];
+    const T* Bb = reinterpret_cast<const T*>(a.B) + ((size_t)ti.slot * a.out_f + f) * a.R;
+    for (int p0 = 0; p0 < npass; p0 += 2) {
+        if (p0 > 0) {
 #pragma unroll
-    for (int i = 0; i < kRows; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            delta[i][e] = 0.f;
-
-    const int ucol0 = slice_of(a, f0) * a.R;
-    bool mfma_done = false;
-    if constexpr (NH > 0) {
-        if (ti.n > a.valu_max) {
-            // B fragments of this wave's blocks: lane (l16, q) holds
-            // B[fb*16 + l16][16h + 8(q&1) .. +8]
-            const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-            const int l16 = lane & 15, q = lane >> 4;
-            const int nfb = a.ft >> 4;
-            const int nblk = ((ti.n + 15) >> 4) * nfb;
-            const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * a.R;
-            uint4 bfr[8][NH];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int b = w + 4 * i;
-                const int fb = (b < nblk ? b : 0) % nfb;
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    bfr[i][h] = ld16(Bb + (size_t)(fb * 16 + l16) * a.R + 16 * h + 8 * (q & 1));
+            for (int i = 0; i < 2; ++i) {
+                const int row = rr + (p0 + i) * rp;
+                yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(row * a.ldy + f) * E : kOOB);
             }
-            stage_u(a, ti, ucol0, us, part);
-            __syncthreads();
-            mfma_delta<NH>(a, ti, bfr, us, dl, dl_ld);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const int row = rr + i * rp;
-                if (row < ti.n) {
-                    const float* dp = dl + row * dl_ld + 8 * fl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        delta[i][e] = dp[e];
-                }
-            }
-            mfma_done = true;
         }
-    }
-    if (!mfma_done) {
-        stage_u(a, ti, ucol0, us, part);
-        __syncthreads();
-        // VALU: delta[i][ff] = sum_j B[f + ff][j] * u[row_i][j], B read 8 ranks at a time
-        const T* Bb = reinterpret_cast<const T*>(a.B) + ((size_t)ti.slot * a.out_f + f) * a.R;
+        float delta[2][8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                delta[i][e] = 0.f;
         for (int j0 = 0; j0 < a.R; j0 += 8) {
             float bv[8][8];  // [feature][rank]
 #pragma unroll
             for (int ff = 0; ff < 8; ++ff)
                 Vec8<T>::load(Bb + (size_t)ff * a.R + j0, bv[ff]);
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const int row = rr + i * rp;
+            for (int i = 0; i < 2; ++i) {
+                const int row = rr + (p0 + i) * rp;
                 if (row < ti.n) {
                     const float* up = us + row * a.R + j0;
                     float uv[8];
@@ -735,18 +782,50 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
                 }
             }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        const int row = rr + i * rp;
-        if (row < ti.n) {
-            float out[8];
-            Vec8<T>::unpack(yraw[i], out);
+        for (int i = 0; i < 2; ++i) {
+            const int row = rr + (p0 + i) * rp;
+            if (row < ti.n) {
+                float out[8];
+                Vec8<T>::unpack(yraw[i], out);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                out[e] += delta[i][e];
-            Vec8<T>::store_buf(yb, (uint32_t)(row * a.ldy + f) * E, out);
+                for (int e = 0; e < 8; ++e)
+                    out[e] += delta[i][e];
+                Vec8<T>::store_buf(yb, (uint32_t)(row * a.ldy + f) * E, out);
+            }
         }
+    }
+}
+
+// One workgroup per (token tile, feature tile); the feature tile lies in one
+// slice.  NH = R / 16 when the MFMA path may run (bf16, R <= 64, slice widths
+// multiple of 32); NH = 0 builds the VALU path alone.  MODE as for the shrink.
+template <typename T, int NH, int MODE>
+__global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
+{
+    constexpr int E = sizeof(T);
+    extern __shared__ float smem[];
+    float* us = smem;                                             // [kTileM][R]
+    float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads]
+
+    const int lin = blockIdx.x;
+    const int ftile = lin % a.n_ftiles;
+    const int tile = lin / a.n_ftiles;
+    TileInfo ti;
+    if (!locate_tile(a.r, tile, ti))
+        return;
+    const int f0 = ftile * a.ft;
+    const int ucol0 = slice_of(a, f0) * a.R;
+    const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
+    if constexpr (NH > 0 && MODE == kMfmaOnly) {
+        expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part);
+    } else if constexpr (NH > 0 && MODE == kMixed) {
+        if (ti.glen > a.valu_max)
+            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part);
+        else
+            expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
+    } else {
+        expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
     }
 }
 
@@ -774,34 +853,103 @@ int valu_max_for(int path, bool mfma_ok, int dflt_auto)
     return dflt_auto;
 }
 
-template <typename T>
-hipError_t launch_shrink(const ShrinkArgs& a, int nb, int grid, hipStream_t st)
+template <typename T, int MODE>
+hipError_t launch_shrink_mode(const ShrinkArgs& a, int nb, int grid, hipStream_t st)
 {
     switch (nb) {
-    case 1: hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((shrink_kernel<T, 3>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((shrink_kernel<T, 4>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((shrink_kernel<T, 1, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_kernel<T, 2, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((shrink_kernel<T, 3, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_kernel<T, 4, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_shrink(bool bf16, int mode, const ShrinkArgs& a, int nb, int grid, hipStream_t st)
+{
+    if (!bf16)
+        return launch_shrink_mode<float, kValuOnly>(a, nb, grid, st);
+    if (mode == kMfmaOnly)
+        return launch_shrink_mode<uint16_t, kMfmaOnly>(a, nb, grid, st);
+    if (mode == kValuOnly)
+        return launch_shrink_mode<uint16_t, kValuOnly>(a, nb, grid, st);
+    return launch_shrink_mode<uint16_t, kMixed>(a, nb, grid, st);
+}
+
+// Path mode of a launch: forced paths map to one variant; AUTO with a host
+// copy of the routing looks at the group lengths (VALU for groups of at most
+// valu_max tokens) and picks a single-path variant when all groups agree.
+int pick_mode(int path, bool mfma_ok, int valu_max, const RouteArgs& r)
+{
+    if (!mfma_ok || path == LORA_PATH_VALU)
+        return kValuOnly;
+    if (path == LORA_PATH_MFMA)
+        return kMfmaOnly;
+    if (!r.kr)
+        return kMixed;
+    bool any_short = false, any_long = false;
+    for (int g = 0; g < r.G; ++g) {
+        const int len = r.k_offs[g + 1] - r.k_offs[g];
+        if (len == 0)
+            continue;
+        if (len > valu_max)
+            any_long = true;
+        else
+            any_short = true;
+    }
+    if (!any_short)
+        return kMfmaOnly;
+    if (!any_long)
+        return kValuOnly;
+    return kMixed;
 }
 
 struct Common {
     FamilyShape fs;
     bool bf16;
+    RouteArgs r;
 };
 
-lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path, int32_t num_groups,
-                           int64_t end, Common* c)
+// Checks dims, family, path and the routing; fills the kernels' routing
+// arguments (with the host copy of the routing when one is given).
+lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path,
+                           const lora_routing_t* rt, Common* c)
 {
     lora_status_t st = family_shape(dims, family, &c->fs);
     if (st != LORA_OK)
         return st;
-    if (path < LORA_PATH_AUTO || path > LORA_PATH_MFMA)
+    if (path < LORA_PATH_AUTO || path > LORA_PATH_MFMA || !rt)
         return LORA_ERR_INVALID_ARGUMENT;
     c->bf16 = dims->dtype == LORA_DTYPE_BF16;
-    if (end < 0 || end > 2147483647LL || num_groups < 0 || num_groups > c->fs.L)
+    const int64_t end = rt->end;
+    const int G = rt->num_groups;
+    if (end < 0 || end > 2147483647LL || G < 0 || G > c->fs.L)
         return LORA_ERR_INVALID_ARGUMENT;
+    RouteArgs& r = c->r;
+    memset(&r, 0, sizeof(r));
+    r.ids = rt->lora_ids;
+    r.offs = rt->grouped_offsets;
+    r.G = G;
+    r.end = (int)end;
+    r.L = c->fs.L;
+    const bool host = rt->host_lora_ids && rt->host_grouped_offsets && G <= LORA_MAX_HOST_GROUPS;
+    if (end > 0 && G > 0 && !host && (!rt->lora_ids || !rt->grouped_offsets))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (host) {
+        const int32_t* o = rt->host_grouped_offsets;
+        if (o[0] != 0 || o[G] != end)
+            return LORA_ERR_INVALID_ARGUMENT;
+        for (int g = 0; g < G; ++g) {
+            if (o[g + 1] < o[g])
+                return LORA_ERR_INVALID_ARGUMENT;
+            if (rt->host_lora_ids[g] < 0 || rt->host_lora_ids[g] >= c->fs.L)
+                return LORA_ERR_SLOT_OUT_OF_RANGE;
+            r.k_ids[g] = rt->host_lora_ids[g];
+        }
+        for (int g = 0; g <= G; ++g)
+            r.k_offs[g] = o[g];
+        r.kr = 1;
+    }
     return LORA_OK;
 }
 
@@ -809,48 +957,42 @@ bool shrink_mfma_ok(const Common& c) { return c.bf16; }
 
 bool expand_mfma_ok(const Common& c)
 {
-    bool widths16 = true;
+    bool widths32 = true;
     for (int s = 0; s < c.fs.n_s; ++s)
-        widths16 = widths16 && c.fs.widths[s] % 16 == 0;
-    return c.bf16 && c.fs.R % 16 == 0 && c.fs.R <= 64 && widths16;
+        widths32 = widths32 && c.fs.widths[s] % 32 == 0;
+    return c.bf16 && c.fs.R % 16 == 0 && c.fs.R <= 64 && widths32;
 }
 
 // shrink launch; `out` receives u (S == 1) or the S slabs
 lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x, int64_t ldx,
-                         const void* A_stack, const int32_t* ids, const int32_t* offs, int G,
-                         int64_t end, float* out, int32_t path, hipStream_t s)
+                         const void* A_stack, float* out, int32_t path, hipStream_t s)
 {
     ShrinkArgs a;
     a.x = x;
     a.ldx = ldx;
     a.A = A_stack;
     a.out = out;
-    a.slab = end * c.fs.C;
-    a.ids = ids;
-    a.offs = offs;
+    a.slab = (int64_t)c.r.end * c.fs.C;
     a.in_f = c.fs.in_f;
     a.C = c.fs.C;
-    a.L = c.fs.L;
-    a.G = G;
-    a.end = (int)end;
     a.S = plan.S;
     a.kc = plan.kc;
     a.nz = plan.nz;
     a.cb = plan.cb;
     a.valu_max = valu_max_for(path, shrink_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_SHRINK", 8));
+    a.r = c.r;
     const int64_t grid = (int64_t)plan.n_tiles * plan.S * plan.nz;
     if (grid > 2147483647LL)
         return LORA_ERR_INVALID_ARGUMENT;
-    const hipError_t e = c.bf16 ? launch_shrink<uint16_t>(a, plan.cb / 16, (int)grid, s)
-                                : launch_shrink<float>(a, plan.cb / 16, (int)grid, s);
+    const int mode = pick_mode(path, shrink_mfma_ok(c), a.valu_max, c.r);
+    const hipError_t e = launch_shrink(c.bf16, mode, a, plan.cb / 16, (int)grid, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
 bool nh_possible(const Common& c, const ExpandArgs& a) { return expand_mfma_ok(c) && a.valu_max < kTileM; }
 
 lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, const void* B_stack,
-                         const int32_t* ids, const int32_t* offs, int G, int64_t end, void* y,
-                         int64_t ldy, int32_t path, hipStream_t s)
+                         void* y, int64_t ldy, int32_t path, hipStream_t s)
 {
     ExpandArgs a;
     a.u = u;
@@ -859,13 +1001,8 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     a.B = B_stack;
     a.y = y;
     a.ldy = ldy;
-    a.ids = ids;
-    a.offs = offs;
     a.C = c.fs.C;
     a.R = c.fs.R;
-    a.L = c.fs.L;
-    a.G = G;
-    a.end = (int)end;
     a.n_s = c.fs.n_s;
     a.out_f = c.fs.out_f;
     for (int i = 0; i < 5; ++i)
@@ -873,27 +1010,42 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     a.ft = expand_tile(c.fs);
     a.n_ftiles = c.fs.out_f / a.ft;
     a.valu_max = valu_max_for(path, expand_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_EXPAND", 8));
-    const int64_t tiles = (end + kTileM - 1) / kTileM + G;
+    a.r = c.r;
+    const int64_t tiles = ((int64_t)c.r.end + kTileM - 1) / kTileM + c.r.G;
     const int64_t grid = tiles * a.n_ftiles;
     if (grid > 2147483647LL)
         return LORA_ERR_INVALID_ARGUMENT;
-    const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4) +
-                       (nh_possible(c, a) ? (size_t)kTileM * (a.ft + kDeltaPad) * sizeof(float) : 0);
+    const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4);
     const dim3 g((unsigned)grid), b(kThreads);
     const int nh = nh_possible(c, a) ? c.fs.R / 16 : 0;
-    if (!c.bf16)
-        hipLaunchKernelGGL((expand_kernel<float, 0>), g, b, lds, s, a);
-    else if (nh == 1)
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 1>), g, b, lds, s, a);
-    else if (nh == 2)
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 2>), g, b, lds, s, a);
-    else if (nh == 3)
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 3>), g, b, lds, s, a);
-    else if (nh == 4)
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 4>), g, b, lds, s, a);
-    else
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 0>), g, b, lds, s, a);
+    const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
+#define LORA_EXPAND_NH(NHV)                                                                       \
+    if (mode == kMfmaOnly)                                                                        \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMfmaOnly>), g, b, lds, s, a);           \
+    else if (mode == kValuOnly)                                                                   \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly>), g, b, lds, s, a);             \
+    else                                                                                          \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMixed>), g, b, lds, s, a);
+    if (!c.bf16) {
+        hipLaunchKernelGGL((expand_kernel<float, 0, kValuOnly>), g, b, lds, s, a);
+    } else if (nh == 1) {
+        LORA_EXPAND_NH(1)
+    } else if (nh == 2) {
+        LORA_EXPAND_NH(2)
+    } else if (nh == 3) {
+        LORA_EXPAND_NH(3)
+    } else if (nh == 4) {
+        LORA_EXPAND_NH(4)
+    } else {
+        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly>), g, b, lds, s, a);
+    }
+#undef LORA_EXPAND_NH
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
+bool row_ok(int64_t ld, int64_t width, int elem)
+{
+    return ld >= width && (ld * elem) % 16 == 0 && ld * elem <= kMaxRowBytes;
 }
 
 }  // namespace
@@ -904,25 +1056,21 @@ using namespace lora;
 extern "C" {
 
 lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                               const void* A_stack, const int32_t* lora_ids,
-                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
-                               float* u, void* workspace, size_t workspace_bytes, int32_t path,
-                               void* stream)
+                               const void* A_stack, const lora_routing_t* routing, float* u,
+                               void* workspace, size_t workspace_bytes, int32_t path, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, num_groups, end, &c);
+    lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
     if (path == LORA_PATH_MFMA && !shrink_mfma_ok(c))
         return LORA_ERR_INVALID_ARGUMENT;
-    if (end == 0 || num_groups == 0)
+    if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
-    if (!x || !A_stack || !lora_ids || !grouped_offsets || !u)
-        return LORA_ERR_INVALID_ARGUMENT;
-    if (ldx < c.fs.in_f || (ldx * c.fs.elem) % 16 || ldx * c.fs.elem > kMaxRowBytes || !aligned16(x) ||
+    if (!x || !A_stack || !u || !row_ok(ldx, c.fs.in_f, c.fs.elem) || !aligned16(x) ||
         !aligned16(A_stack) || !aligned16(u))
         return LORA_ERR_INVALID_ARGUMENT;
-    const ShrinkPlan plan = plan_shrink(c.fs, end, num_groups);
+    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
     const size_t need = shrink_workspace(plan);
     if (need > 0) {
         if (!workspace || !aligned16(workspace))
@@ -932,78 +1080,70 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* out = plan.S > 1 ? reinterpret_cast<float*>(workspace) : u;
-    st = run_shrink(c, plan, x, ldx, A_stack, lora_ids, grouped_offsets, num_groups, end, out, path, s);
+    st = run_shrink(c, plan, x, ldx, A_stack, out, path, s);
     if (st != LORA_OK || plan.S == 1)
         return st;
-    const int64_t n4 = end * c.fs.C / 4;
+    const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
     hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       s, out, (int64_t)(end * c.fs.C / 4), plan.S, u, n4);
+                       s, out, n4, plan.S, u, n4);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
 lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
-                               const void* B_stack, const int32_t* lora_ids,
-                               const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
-                               void* y, int64_t ldy, int32_t path, void* stream)
+                               const void* B_stack, const lora_routing_t* routing, void* y,
+                               int64_t ldy, int32_t path, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, num_groups, end, &c);
+    lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
     if (path == LORA_PATH_MFMA && !expand_mfma_ok(c))
         return LORA_ERR_INVALID_ARGUMENT;
-    if (end == 0 || num_groups == 0)
+    if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
-    if (!u || !B_stack || !lora_ids || !grouped_offsets || !y)
-        return LORA_ERR_INVALID_ARGUMENT;
-    if (ldy < c.fs.out_f || (ldy * c.fs.elem) % 16 || ldy * c.fs.elem > kMaxRowBytes || !aligned16(u) ||
+    if (!u || !B_stack || !y || !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(u) ||
         !aligned16(B_stack) || !aligned16(y))
         return LORA_ERR_INVALID_ARGUMENT;
-    return run_expand(c, u, 0, 1, B_stack, lora_ids, grouped_offsets, num_groups, end, y, ldy, path,
-                      reinterpret_cast<hipStream_t>(stream));
+    return run_expand(c, u, 0, 1, B_stack, y, ldy, path, reinterpret_cast<hipStream_t>(stream));
 }
 
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                              const void* A_stack, const void* B_stack, const int32_t* lora_ids,
-                              const int32_t* grouped_offsets, int32_t num_groups, int64_t end,
+                              const void* A_stack, const void* B_stack, const lora_routing_t* routing,
                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                               int32_t path, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, num_groups, end, &c);
+    lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
     if (path == LORA_PATH_MFMA && !(shrink_mfma_ok(c) && expand_mfma_ok(c)))
         return LORA_ERR_INVALID_ARGUMENT;
-    if (end == 0 || num_groups == 0)
+    if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
-    if (!x || !A_stack || !B_stack || !lora_ids || !grouped_offsets || !y || !workspace)
+    if (!x || !A_stack || !B_stack || !y || !workspace || !row_ok(ldx, c.fs.in_f, c.fs.elem) ||
+        !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(x) || !aligned16(y) || !aligned16(A_stack) ||
+        !aligned16(B_stack) || !aligned16(workspace))
         return LORA_ERR_INVALID_ARGUMENT;
-    if (ldx < c.fs.in_f || (ldx * c.fs.elem) % 16 || ldy < c.fs.out_f || (ldy * c.fs.elem) % 16 ||
-        ldx * c.fs.elem > kMaxRowBytes || ldy * c.fs.elem > kMaxRowBytes || !aligned16(x) ||
-        !aligned16(y) || !aligned16(A_stack) || !aligned16(B_stack) || !aligned16(workspace))
-        return LORA_ERR_INVALID_ARGUMENT;
-    const ShrinkPlan plan = plan_shrink(c.fs, end, num_groups);
+    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
     if (workspace_bytes < delta_workspace(plan))
         return LORA_ERR_CAPACITY;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* slabs = reinterpret_cast<float*>(workspace);
-    st = run_shrink(c, plan, x, ldx, A_stack, lora_ids, grouped_offsets, num_groups, end, slabs, path, s);
+    st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
     if (st != LORA_OK)
         return st;
     int S = plan.S;
+    const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
     if (S > 1 && env_int("LORA_SGMV_DELTA_REDUCE", 0)) {
         // fold the slabs into slab 0 first (tuning switch: one extra launch,
         // the expand then stages a single slab)
-        const int64_t n4 = end * c.fs.C / 4;
         hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
                            0, s, slabs, n4, S, slabs, n4);
         if (hipGetLastError() != hipSuccess)
             return LORA_ERR_DEVICE;
         S = 1;
     }
-    return run_expand(c, slabs, end * c.fs.C, S, B_stack, lora_ids, grouped_offsets, num_groups, end,
-                      y, ldy, path, s);
+    return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, y, ldy, path, s);
 }
 
 }  // extern "C"

@@ -97,9 +97,9 @@ class GpuLayer:
         self.end = self.rt["end"]
         self.G = self.rt["num_groups"]
         self.st = {k: to_dev(v, w.dtype) for k, v in stacks.items()}
-        ids = self.rt["lora_ids"] if self.G else np.zeros(1, np.int32)
-        self.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
-        self.goffs = torch.from_numpy(np.ascontiguousarray(self.rt["grouped_offsets"], np.int32)).cuda()
+        # routing with host copies (kernel-argument routing) and device-only
+        self.routing = {"host": srg.LoraRouting.from_host(self.rt, host_copy=True),
+                        "device": srg.LoraRouting.from_host(self.rt, host_copy=False)}
         self.dev = {}
         self.shape = {}
         for fam, xk, yk in ((srg.FAMILY_QKV, "x_qkv", "y_qkv"), (srg.FAMILY_O, "x_o", "y_o")):
@@ -124,23 +124,22 @@ class GpuLayer:
             self.ws[fam] = torch.full((max(nb, 16) // 4 + 4,), -1, dtype=torch.int32, device="cuda")
 
     def run(self, path: int = srg.PATH_AUTO, families=(srg.FAMILY_QKV, srg.FAMILY_O),
-            fused: bool = False):
+            fused: bool = False, routing: str = "host"):
         """fused=False: lora_sgmv_shrink then lora_sgmv_expand (u checked);
-        fused=True: lora_sgmv_delta (u stays internal)."""
+        fused=True: lora_sgmv_delta (u stays internal).  routing: "host"
+        (host copies passed, kernel-argument routing) or "device"."""
+        rt = self.routing[routing]
         for fam in families:
             xk, yk = ("x_qkv", "y_qkv") if fam == srg.FAMILY_QKV else ("x_o", "y_o")
             A = self.st["A_qkv" if fam == srg.FAMILY_QKV else "A_o"]
             B = self.st["B_qkv" if fam == srg.FAMILY_QKV else "B_o"]
             if fused:
-                log(f"  launch delta family={fam} path={path} end={self.end} G={self.G}")
-                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, self.ids, self.goffs, self.G,
-                                    self.end, self.dev[yk], self.ws[fam], path)
+                log(f"  launch delta family={fam} path={path} routing={routing} end={self.end} G={self.G}")
+                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path)
                 continue
-            log(f"  launch shrink+expand family={fam} path={path} end={self.end} G={self.G}")
-            srg.lora_sgmv_shrink(self.dims, fam, self.dev[xk], A, self.ids, self.goffs, self.G,
-                                 self.end, self.u[fam], self.ws[fam], path)
-            srg.lora_sgmv_expand(self.dims, fam, self.u[fam], B, self.ids, self.goffs, self.G,
-                                 self.end, self.dev[yk], path)
+            log(f"  launch shrink+expand family={fam} path={path} routing={routing} end={self.end} G={self.G}")
+            srg.lora_sgmv_shrink(self.dims, fam, self.dev[xk], A, rt, self.u[fam], self.ws[fam], path)
+            srg.lora_sgmv_expand(self.dims, fam, self.u[fam], B, rt, self.dev[yk], path)
         import torch
         torch.cuda.synchronize()
 

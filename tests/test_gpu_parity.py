@@ -44,13 +44,14 @@ def workload_case(name, layer=0):
     return _CACHE[key]
 
 
-@pytest.mark.parametrize("api", ["split", "delta", "delta_reduce"])
+@pytest.mark.parametrize("api", ["split", "delta", "delta_reduce", "split_devroute"])
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
 def test_full_workload_parity(name, path, api, monkeypatch):
     """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
     lora_sgmv_delta; delta_reduce: lora_sgmv_delta with its slabs folded by
-    the reduce kernel before the expand."""
+    the reduce kernel before the expand; split_devroute: split with the
+    routing read from the device arrays only."""
     w, lengths, slots, stacks, acts, ref = workload_case(name)
     if path == "mfma" and w.dtype != "bf16":
         pytest.skip("MFMA path is bf16 only")
@@ -58,8 +59,8 @@ def test_full_workload_parity(name, path, api, monkeypatch):
         monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1")
     log(f"[parity] workload={name} path={path} api={api} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(PATHS[path], fused=api != "split")
-    ey, eu = compare(w, gl, ref, check_u=api == "split")
+    gl.run(PATHS[path], fused=api.startswith("delta"), routing="device" if api.endswith("devroute") else "host")
+    ey, eu = compare(w, gl, ref, check_u=api.startswith("split"))
     log(f"[parity] workload={name} path={path} api={api} y_rel={ey:.3e} u_rel={eu:.3e}")
     assert ey <= TOL[w.dtype]
     assert eu <= U_TOL[w.dtype]
@@ -81,7 +82,7 @@ def test_stack_layers_sampled():
                 for i in range(len(lengths))}
         log(f"[stack] layer={layer}")
         gl = GpuLayer(w, stacks, lengths, slots, acts)
-        gl.run(srg.PATH_AUTO, fused=layer % 2 == 1)
+        gl.run(srg.PATH_AUTO, fused=layer % 2 == 1, routing="device" if layer % 3 == 0 else "host")
         ref = oracle_layer(w, stacks, lengths, slots, acts, token_rows=rows)
         ey, eu = compare(w, gl, ref, check_u=layer % 2 == 0)
         worst = max(worst, ey)
@@ -111,9 +112,10 @@ def run_custom(w, lengths, slots, path, ranks=None, targets="qkvo", zero_B=False
     return gl, ref, acts
 
 
+@pytest.mark.parametrize("routing", ["host", "device"])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("path", list(PATHS))
-def test_ragged_segments_around_tile_size(path, fused):
+def test_ragged_segments_around_tile_size(path, fused, routing):
     w = small_bf16(L=8)
     lengths = np.array([1, 15, 16, 17, 63, 64, 65, 127, 129, 3, 0, 200], np.int64)
     slots = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, -1, 3, 1], np.int32)
@@ -121,7 +123,7 @@ def test_ragged_segments_around_tile_size(path, fused):
     stacks = pack_stacks(w, 0, np.full(w.max_num_loras, 8, np.int32))
     acts = synth.draw_activations(w, 0, int(lengths.sum()))
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(PATHS[path], fused=fused)
+    gl.run(PATHS[path], fused=fused, routing=routing)
     ey, eu = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts), check_u=not fused)
     assert ey <= TOL["bf16"] and eu <= U_TOL["bf16"]
 
@@ -229,24 +231,32 @@ def test_host_side_argument_errors_launch_nothing():
     A = torch.zeros((w.max_num_loras, 3 * w.max_lora_rank, w.hidden), dtype=torch.bfloat16, device="cuda")
     ids = torch.zeros(1, dtype=torch.int32, device="cuda")
     offs = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    rt = srg.LoraRouting(ids, offs, 1, 4)
     u = torch.zeros((4, 3 * w.max_lora_rank), dtype=torch.float32, device="cuda")
     # misaligned x (one element in)
     with pytest.raises(srg.LoraError) as e:
-        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x.view(-1)[1:1 + 3 * w.hidden].view(3, w.hidden), A,
-                             ids, offs, 1, 3, u)
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x.view(-1)[1:1 + 3 * w.hidden].view(3, w.hidden), A, rt, u)
     assert e.value.code == 1
     # workspace too small for a split-K launch
     with pytest.raises(srg.LoraError) as e:
-        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, ids, offs, 1, 4, u,
-                             torch.zeros(4, dtype=torch.int32, device="cuda"))
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, rt, u, torch.zeros(4, dtype=torch.int32, device="cuda"))
     assert e.value.code in (1, 4)
     # more groups than slots
     with pytest.raises(srg.LoraError) as e:
-        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, ids, offs, w.max_num_loras + 1, 4, u)
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, srg.LoraRouting(ids, offs, w.max_num_loras + 1, 4), u)
     assert e.value.code == 1
+    # host routing copies that disagree with end, or carry a bad slot id
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, srg.LoraRouting(ids, offs, 1, 4, np.array([0]),
+                                                                      np.array([0, 3])), u)
+    assert e.value.code == 1
+    with pytest.raises(srg.LoraError) as e:
+        srg.lora_sgmv_shrink(d, srg.FAMILY_QKV, x, A, srg.LoraRouting(ids, offs, 1, 4, np.array([w.max_num_loras]),
+                                                                      np.array([0, 4])), u)
+    assert e.value.code == 3
     # MFMA forced on fp32
     d32 = srg.LoraDims(**{**d.__dict__, "dtype": "f32"})
     with pytest.raises(srg.LoraError) as e:
-        srg.lora_sgmv_expand(d32, srg.FAMILY_O, u, A, ids, offs, 1, 4, x, srg.PATH_MFMA)
+        srg.lora_sgmv_expand(d32, srg.FAMILY_O, u, A, rt, x, srg.PATH_MFMA)
     assert e.value.code == 1
     torch.cuda.synchronize()
