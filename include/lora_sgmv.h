@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -73,10 +73,15 @@ enum { LORA_TARGET_Q = 1, LORA_TARGET_K = 2, LORA_TARGET_V = 4, LORA_TARGET_O = 
 
 /* Kernel path selection for the device calls.  AUTO picks per token tile:
  * wavefront-reduction VALU code for short (decode-shaped) tiles, MFMA for
- * longer bf16 tiles.  VALU / MFMA force one path (MFMA needs bf16; for the
- * expand also a rank that is a multiple of 16 and at most 64 and slice widths
- * that are multiples of 32). */
-enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2 };
+ * longer bf16 tiles; for lora_sgmv_delta, when the host copy of the routing
+ * shows only short groups, the one-kernel path below.  VALU / MFMA force one
+ * path (MFMA needs bf16; for the expand also a rank that is a multiple of 16
+ * and at most 64 and slice widths that are multiples of 32).  FUSED (only
+ * lora_sgmv_delta) forces the one-kernel path: shrink and expand of tiles of
+ * at most 16 tokens in one launch, each workgroup recomputing the rank-space
+ * values of its slice; it needs bf16, a rank of 16 or 32 and slice widths
+ * that are multiples of 32, and uses no workspace. */
+enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2, LORA_PATH_FUSED = 3 };
 
 /* Model and LoRA capacity dimensions.  max_lora_rank (R) and max_num_loras (L)
  * correspond to LoRAConfig.max_lora_rank / max_num_loras ([MAX-lora] LoRAConfig
@@ -269,6 +274,8 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  * are neither read nor written.  Arguments as for lora_sgmv_shrink and
  * lora_sgmv_expand; workspace >= lora_sgmv_workspace_bytes(dims, family, end)
  * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
+ * path: any LORA_PATH_*; with the one-kernel path (FUSED, or AUTO on short
+ * groups) the workspace is not touched and y must not alias x or the stacks.
  */
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
                               const void* A_stack, const void* B_stack, const lora_routing_t* routing,

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     FAMILY_O,
     FAMILY_QKV,
     PATH_AUTO,
+    PATH_FUSED,
     PATH_MFMA,
     PATH_VALU,
     MAX_HOST_GROUPS,

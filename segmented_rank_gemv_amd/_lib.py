@@ -14,7 +14,7 @@ _LIB_PATH = os.path.join(_PKG, "liblora_sgmv.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FAMILY_QKV, FAMILY_O = 0, 1
-PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_FUSED = 0, 1, 2, 3
 _TARGET_BITS = {"q": 1, "k": 2, "v": 4, "o": 8}
 _DTYPES = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
 

@@ -225,12 +225,15 @@ struct RouteArgs {
     int k_ids[LORA_MAX_HOST_GROUPS];
 };
 
-// Locate token tile `tile`: groups are cut into kTileM-token tiles in group
-// order.  Every lane takes one group, a wave-wide inclusive scan of the
-// per-group tile counts gives each group's first tile and a ballot finds the
-// group holding `tile`.  Offsets are clamped into [0, end] and made
-// non-decreasing per group, so malformed routing cannot move accesses outside
-// rows [0, end).  Returns false past the last tile or for a bad slot id.
+// Locate token tile `tile`: groups are cut into tiles of at most TM tokens
+// in group order (BAL: a group of n tokens becomes ceil(n / TM) tiles of
+// near-equal size; otherwise TM-token tiles and a shorter last one).  Every
+// lane takes one group, a wave-wide inclusive scan of the per-group tile
+// counts gives each group's first tile and a ballot finds the group holding
+// `tile`.  Offsets are clamped into [0, end] and made non-decreasing per
+// group, so malformed routing cannot move accesses outside rows [0, end).
+// Returns false past the last tile or for a bad slot id.
+template <int TM, bool BAL>
 __device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
 {
     const int lane = threadIdx.x & 63;
@@ -244,18 +247,28 @@ __device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
             s = min(max(o0, 0), r.end);
             e = min(max(o1, s), r.end);
         }
-        const int nt = (e - s + kTileM - 1) / kTileM;
+        const int nt = (e - s + TM - 1) / TM;
         const int incl = wave_incl_scan(nt);
         const unsigned long long hit = __ballot(i < r.G && base + incl > tile);
         if (hit) {
             const int src = __ffsll((long long)hit) - 1;
             const int gs = __shfl(s, src, 64), ge = __shfl(e, src, 64);
-            const int first = base + __shfl(incl, src, 64) - __shfl(nt, src, 64);
+            const int gnt = __shfl(nt, src, 64);
+            const int first = base + __shfl(incl, src, 64) - gnt;
+            const int j = tile - first, len = ge - gs;
+            int t0, t1;
+            if (BAL) {
+                t0 = gs + (int)(((int64_t)len * j) / gnt);
+                t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
+            } else {
+                t0 = gs + j * TM;
+                t1 = min(t0 + TM, ge);
+            }
             // wave-uniform values: keep them in scalar registers
             ti.g = __builtin_amdgcn_readfirstlane(c0 + src);
-            ti.t0 = __builtin_amdgcn_readfirstlane(gs + (tile - first) * kTileM);
-            ti.n = __builtin_amdgcn_readfirstlane(min(kTileM, ge - gs - (tile - first) * kTileM));
-            ti.glen = __builtin_amdgcn_readfirstlane(ge - gs);
+            ti.t0 = __builtin_amdgcn_readfirstlane(t0);
+            ti.n = __builtin_amdgcn_readfirstlane(t1 - t0);
+            ti.glen = __builtin_amdgcn_readfirstlane(len);
             ti.slot = __builtin_amdgcn_readfirstlane(r.kr ? r.k_ids[ti.g] : r.ids[ti.g]);
             return ti.slot >= 0 && ti.slot < r.L;
         }
@@ -488,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
     const int s = (lin / a.nz) % a.S;
     const int tile = lin / (a.nz * a.S);
     TileInfo ti;
-    if (!locate_tile(a.r, tile, ti))
+    if (!locate_tile<kTileM, false>(a.r, tile, ti))
         return;
     const int k0 = s * a.kc, k1 = min(k0 + a.kc, a.in_f);
     const int c0 = z * a.cb, c1 = min(c0 + a.cb, a.C);
@@ -812,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     const int ftile = lin % a.n_ftiles;
     const int tile = lin / a.n_ftiles;
     TileInfo ti;
-    if (!locate_tile(a.r, tile, ti))
+    if (!locate_tile<kTileM, false>(a.r, tile, ti))
         return;
     const int f0 = ftile * a.ft;
     const int ucol0 = slice_of(a, f0) * a.R;
@@ -827,6 +840,171 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     } else {
         expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
     }
+}
+
+// ---------------------------------------------------------------------------
+// one-kernel delta for short groups (decode batches)
+//
+// A decode batch moves a few MB per family, so a launch and a round trip to
+// memory cost more than the transfer itself; the split-K shrink followed by
+// the expand pays two of each and moves the split partial sums through
+// memory.  Here one workgroup owns a tile of at most 16 tokens of one group,
+// one slice (R columns of u) and one feature tile of that slice.  Its 16
+// waves split K; every wave issues all its loads (x rows, A rows, its y run
+// and B rows) at once, computes its K share of u with MFMA, and the 16
+// partial u tiles are summed in LDS in wave order.  The waves then expand u
+// into their 32-feature pair of y.  Each workgroup recomputes u for its
+// slice: A and x are re-read from L2 once per feature tile, traded for the
+// second launch and round trip.  Workgroups of one token tile are placed on
+// one XCD (consecutive workgroups go to consecutive XCDs), so the tile's x
+// rows and the group's A rows are fetched into that XCD's L2 once.
+
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedTileM = 16;
+constexpr int kFusedMaxFeat = 32 * kFusedWaves;  // one 32-feature pair per wave
+constexpr int kXcds = 8;
+
+struct FusedArgs {
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* A;  // [L][C][in_f]
+    const uint16_t* B;  // [L][out_f][R]
+    uint16_t* y;
+    int64_t ldy;
+    int in_f, C, out_f, n_s;
+    int soff[5];
+    int nft[4];      // feature tiles per slice
+    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat)
+    int nf;          // feature tiles per token tile
+    int wave_steps;  // 32-element K steps per wave
+    RouteArgs r;
+};
+
+// STEPS = K steps a wave keeps in flight per batch (register budget).
+template <int NH, int STEPS>
+__global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
+{
+    constexpr int R = 16 * NH;
+    __shared__ float part[kFusedWaves * kFusedTileM * R];  // per-wave partial u
+    __shared__ float us[kFusedTileM * R];                  // u of the tile
+
+    const int b = blockIdx.x;
+    const int k = b / kXcds;
+    const int tile = (k / a.nf) * kXcds + b % kXcds;
+    const int ftile = k % a.nf;
+    TileInfo ti;
+    if (!locate_tile<kFusedTileM, true>(a.r, tile, ti))
+        return;
+    int sl = 0, rem = ftile;
+    while (sl < a.n_s - 1 && rem >= a.nft[sl]) {
+        rem -= a.nft[sl];
+        ++sl;
+    }
+    const int f0 = a.soff[sl] + rem * a.F;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q = lane >> 4;
+
+    // --- issue the loads: the wave's y run and B rows, then x / A batches
+    const int np = a.F >> 5;
+    const bool pair = w < np;
+    const bool tok = l16 < ti.n;
+    const Buf yb(a.y + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * 2));
+    const uint32_t yoff = (pair && tok) ? (uint32_t)(l16 * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
+    const uint4 yraw = yb.ld16(yoff);
+    // B rows as the M operand, permuted: row i of block h is feature
+    // 32 w + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
+    const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, (uint32_t)(a.F * R * 2));
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);
+    uint4 bfr[2][NH];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kh = 0; kh < NH; ++kh)
+            bfr[h][kh] = bb.ld16(pair ? (uint32_t)((32 * w + mrow + 4 * h) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+
+    // --- u partial over the wave's K range: x rows as M, A rows as N.  K
+    // positions past the wave's range read as zero (offset kOOB).
+    const Buf xb(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));  // rows >= n read zero
+    const Buf ab(a.A + ((size_t)ti.slot * a.C + sl * R) * a.in_f, (uint32_t)(R * a.in_f * 2));
+    const int kw0 = w * a.wave_steps * 32;
+    const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
+    const uint32_t xrow = (uint32_t)(l16 * a.ldx) * 2, arow = (uint32_t)(l16 * a.in_f) * 2;
+    f32x4_t acc[NH];
+#pragma unroll
+    for (int nb = 0; nb < NH; ++nb)
+        acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
+    for (int bt = 0; bt < nbatch; ++bt) {
+        uint4 xr[STEPS], ar[STEPS][NH];
+#pragma unroll
+        for (int i = 0; i < STEPS; ++i) {
+            const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
+            const uint32_t ko = kk < kw1 ? (uint32_t)kk * 2 : kOOB;
+            xr[i] = xb.ld16(xrow + ko);
+#pragma unroll
+            for (int nb = 0; nb < NH; ++nb)
+                ar[i][nb] = ab.ld16(arow + (uint32_t)(nb * 16 * a.in_f) * 2 + ko);
+        }
+        // keep every load of the batch ahead of the first MFMA: one round trip
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < STEPS; ++i)
+#pragma unroll
+            for (int nb = 0; nb < NH; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
+                                                                  __builtin_bit_cast(bf16x8_t, ar[i][nb]),
+                                                                  acc[nb], 0, 0, 0);
+    }
+    // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
+#pragma unroll
+    for (int nb = 0; nb < NH; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            part[(w * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < kFusedTileM * R; e += kFusedThreads) {
+        float v = part[e];
+#pragma unroll
+        for (int ww = 1; ww < kFusedWaves; ++ww)
+            v += part[ww * kFusedTileM * R + e];
+        us[e] = v;
+    }
+    __syncthreads();
+    if (!pair)
+        return;
+
+    // --- expand: u = hi + lo in bf16 as the N operand (tokens), y as C
+    bf16x8_t uf[NH];
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) {
+        const float* up = us + l16 * R + 16 * kh + 8 * (q & 1);
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = up[2 * e], v1 = up[2 * e + 1];
+            uint32_t hi = f2bf_pair(v0, v1);
+            if (q >= 2)
+                hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+            pk[e] = hi;
+        }
+        uf[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+    f32x4_t acc0 = {bf2f(yraw.x & 0xFFFFu), bf2f(yraw.x >> 16), bf2f(yraw.y & 0xFFFFu), bf2f(yraw.y >> 16)};
+    f32x4_t acc1 = {bf2f(yraw.z & 0xFFFFu), bf2f(yraw.z >> 16), bf2f(yraw.w & 0xFFFFu), bf2f(yraw.w >> 16)};
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[0][kh]), uf[kh], acc0, 0,
+                                                      0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[1][kh]), uf[kh], acc1, 0,
+                                                      0, 0);
+    }
+    uint4 o;
+    o.x = f2bf_pair(acc0[0], acc0[1]);
+    o.y = f2bf_pair(acc0[2], acc0[3]);
+    o.z = f2bf_pair(acc1[0], acc1[1]);
+    o.w = f2bf_pair(acc1[2], acc1[3]);
+    yb.st16(yoff, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -918,7 +1096,7 @@ lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path
     lora_status_t st = family_shape(dims, family, &c->fs);
     if (st != LORA_OK)
         return st;
-    if (path < LORA_PATH_AUTO || path > LORA_PATH_MFMA || !rt)
+    if (path < LORA_PATH_AUTO || path > LORA_PATH_FUSED || !rt)
         return LORA_ERR_INVALID_ARGUMENT;
     c->bf16 = dims->dtype == LORA_DTYPE_BF16;
     const int64_t end = rt->end;
@@ -1043,6 +1221,78 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
+// One-kernel delta: bf16, R = 16 or 32, slice widths multiples of 32.
+bool fused_ok(const Common& c)
+{
+    bool widths32 = true;
+    for (int s = 0; s < c.fs.n_s; ++s)
+        widths32 = widths32 && c.fs.widths[s] % 32 == 0;
+    return c.bf16 && (c.fs.R == 16 || c.fs.R == 32) && widths32;
+}
+
+// AUTO takes the one-kernel delta when the host copy of the routing shows
+// that no group is longer than LORA_SGMV_FUSED_MAX tokens (default 32).
+bool fused_auto(const Common& c)
+{
+    if (!fused_ok(c) || !c.r.kr)
+        return false;
+    const int lim = env_int("LORA_SGMV_FUSED_MAX", 32);
+    for (int g = 0; g < c.r.G; ++g)
+        if (c.r.k_offs[g + 1] - c.r.k_offs[g] > lim)
+            return false;
+    return true;
+}
+
+lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void* A_stack, const void* B_stack,
+                        void* y, int64_t ldy, hipStream_t s)
+{
+    FusedArgs a;
+    a.x = reinterpret_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.A = reinterpret_cast<const uint16_t*>(A_stack);
+    a.B = reinterpret_cast<const uint16_t*>(B_stack);
+    a.y = reinterpret_cast<uint16_t*>(y);
+    a.ldy = ldy;
+    a.in_f = c.fs.in_f;
+    a.C = c.fs.C;
+    a.out_f = c.fs.out_f;
+    a.n_s = c.fs.n_s;
+    for (int i = 0; i < 5; ++i)
+        a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
+    // feature tile: the largest power of two <= kFusedMaxFeat dividing every slice width
+    int F = kFusedMaxFeat;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        while (c.fs.widths[sl] % F)
+            F >>= 1;
+    a.F = F;
+    a.nf = 0;
+    for (int sl = 0; sl < 4; ++sl) {
+        a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / F : 0;
+        a.nf += a.nft[sl];
+    }
+    const int steps = (c.fs.in_f + 31) / 32;
+    a.wave_steps = (steps + kFusedWaves - 1) / kFusedWaves;
+    a.r = c.r;
+    // token tiles: exact count from the host routing, else a bound
+    int64_t tiles = 0;
+    if (c.r.kr) {
+        for (int g = 0; g < c.r.G; ++g)
+            tiles += (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM;
+    } else {
+        tiles = ((int64_t)c.r.end + kFusedTileM - 1) / kFusedTileM + c.r.G;
+    }
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds * a.nf;
+    if (grid == 0)
+        return LORA_OK;
+    if (grid > 2147483647LL)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (c.fs.R == 16)
+        hipLaunchKernelGGL((fused_delta_kernel<1, 8>), dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((fused_delta_kernel<2, 4>), dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
 bool row_ok(int64_t ld, int64_t width, int elem)
 {
     return ld >= width && (ld * elem) % 16 == 0 && ld * elem <= kMaxRowBytes;
@@ -1063,7 +1313,7 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
     lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
-    if (path == LORA_PATH_MFMA && !shrink_mfma_ok(c))
+    if ((path == LORA_PATH_MFMA && !shrink_mfma_ok(c)) || path == LORA_PATH_FUSED)
         return LORA_ERR_INVALID_ARGUMENT;
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
@@ -1097,7 +1347,7 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
     lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
-    if (path == LORA_PATH_MFMA && !expand_mfma_ok(c))
+    if ((path == LORA_PATH_MFMA && !expand_mfma_ok(c)) || path == LORA_PATH_FUSED)
         return LORA_ERR_INVALID_ARGUMENT;
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
@@ -1116,7 +1366,8 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
     lora_status_t st = check_common(dims, family, path, routing, &c);
     if (st != LORA_OK)
         return st;
-    if (path == LORA_PATH_MFMA && !(shrink_mfma_ok(c) && expand_mfma_ok(c)))
+    if ((path == LORA_PATH_MFMA && !(shrink_mfma_ok(c) && expand_mfma_ok(c))) ||
+        (path == LORA_PATH_FUSED && !fused_ok(c)))
         return LORA_ERR_INVALID_ARGUMENT;
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
@@ -1128,6 +1379,8 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
     if (workspace_bytes < delta_workspace(plan))
         return LORA_ERR_CAPACITY;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c)))
+        return run_fused(c, x, ldx, A_stack, B_stack, y, ldy, s);
     float* slabs = reinterpret_cast<float*>(workspace);
     st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
     if (st != LORA_OK)

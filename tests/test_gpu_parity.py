@@ -28,7 +28,14 @@ def _need_gpu():
 
 
 PATHS = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA}
+DELTA_PATHS = {**PATHS, "fused": srg.PATH_FUSED}
 _CACHE = {}
+
+
+def fused_applies(w) -> bool:
+    """The one-kernel delta needs bf16 and a rank of 16 or 32 (every
+    workload here has slice widths that are multiples of 32)."""
+    return w.dtype == "bf16" and w.max_lora_rank in (16, 32)
 
 
 def workload_case(name, layer=0):
@@ -45,21 +52,28 @@ def workload_case(name, layer=0):
 
 
 @pytest.mark.parametrize("api", ["split", "delta", "delta_reduce", "split_devroute"])
-@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("path", list(DELTA_PATHS))
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
 def test_full_workload_parity(name, path, api, monkeypatch):
     """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
-    lora_sgmv_delta; delta_reduce: lora_sgmv_delta with its slabs folded by
-    the reduce kernel before the expand; split_devroute: split with the
-    routing read from the device arrays only."""
+    lora_sgmv_delta (AUTO takes the one-kernel path on decode batches);
+    delta_reduce: lora_sgmv_delta on the two-kernel path with its slabs folded
+    by the reduce kernel before the expand; split_devroute: split with the
+    routing read from the device arrays only.  path fused: lora_sgmv_delta
+    forced onto the one-kernel path."""
     w, lengths, slots, stacks, acts, ref = workload_case(name)
     if path == "mfma" and w.dtype != "bf16":
         pytest.skip("MFMA path is bf16 only")
+    if path == "fused" and api != "delta":
+        pytest.skip("the one-kernel path exists for lora_sgmv_delta only")
+    if path == "fused" and not fused_applies(w):
+        pytest.skip("one-kernel path needs bf16 and rank 16 or 32 (error path tested separately)")
     if api == "delta_reduce":
         monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1")
+        monkeypatch.setenv("LORA_SGMV_FUSED_MAX", "0")
     log(f"[parity] workload={name} path={path} api={api} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(PATHS[path], fused=api.startswith("delta"), routing="device" if api.endswith("devroute") else "host")
+    gl.run(DELTA_PATHS[path], fused=api.startswith("delta"), routing="device" if api.endswith("devroute") else "host")
     ey, eu = compare(w, gl, ref, check_u=api.startswith("split"))
     log(f"[parity] workload={name} path={path} api={api} y_rel={ey:.3e} u_rel={eu:.3e}")
     assert ey <= TOL[w.dtype]
@@ -114,8 +128,10 @@ def run_custom(w, lengths, slots, path, ranks=None, targets="qkvo", zero_B=False
 
 @pytest.mark.parametrize("routing", ["host", "device"])
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("path", list(DELTA_PATHS))
 def test_ragged_segments_around_tile_size(path, fused, routing):
+    if path == "fused" and not fused:
+        pytest.skip("the one-kernel path exists for lora_sgmv_delta only")
     w = small_bf16(L=8)
     lengths = np.array([1, 15, 16, 17, 63, 64, 65, 127, 129, 3, 0, 200], np.int64)
     slots = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, -1, 3, 1], np.int32)
@@ -123,9 +139,64 @@ def test_ragged_segments_around_tile_size(path, fused, routing):
     stacks = pack_stacks(w, 0, np.full(w.max_num_loras, 8, np.int32))
     acts = synth.draw_activations(w, 0, int(lengths.sum()))
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(PATHS[path], fused=fused, routing=routing)
+    gl.run(DELTA_PATHS[path], fused=fused, routing=routing)
     ey, eu = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts), check_u=not fused)
     assert ey <= TOL["bf16"] and eu <= U_TOL["bf16"]
+
+
+@pytest.mark.parametrize("R", [16, 32])
+@pytest.mark.parametrize("path", ["fused", "auto"])
+def test_one_kernel_delta_odd_widths_and_long_k(R, path):
+    """One-kernel delta on shapes that exercise its tiling: K = 4640 (QKV) and
+    4608 (O) give more K steps per wave than one batch and a K tail; slice
+    widths 4608 / 1152 / 1152 and an o_proj width of 4640 give feature tiles
+    of 128 and 32.  Groups of 1..33 tokens (balanced 16-token tiles), a base
+    request and an empty one; AUTO takes the one-kernel path since no group
+    is longer than 32 (except the 33-token one, which sends AUTO to the
+    two-kernel path)."""
+    base = synth.get_workload("decode")
+    w = synth.Workload(**{**base.__dict__, "hidden": 4640, "n_heads": 16, "n_kv_heads": 4,
+                          "head_dim": 288, "max_lora_rank": R, "max_num_loras": 6})
+    lengths = np.array([1, 2, 16, 17, 31, 33, 5, 0, 9], np.int64)
+    slots = np.array([0, 1, 2, 3, 4, 5, -1, 0, 1], np.int32)
+    if path == "auto":
+        lengths = lengths[lengths != 33]
+        slots = slots[:len(lengths)]
+    stacks = pack_stacks(w, 0, np.array([R, R // 2, 8, R, 8, R], np.int32))
+    acts = synth.draw_activations(w, 0, int(lengths.sum()))
+    log(f"[one-kernel] R={R} path={path}")
+    gl = GpuLayer(w, stacks, lengths, slots, acts)
+    gl.run(DELTA_PATHS[path], fused=True)
+    ey, _ = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts), check_u=False)
+    log(f"[one-kernel] R={R} path={path} y_rel={ey:.3e}")
+    assert ey <= TOL["bf16"]
+
+
+def test_one_kernel_path_rejected_where_it_does_not_apply():
+    """PATH_FUSED: an error (no launch) for fp32, for rank 64 and for the
+    split calls; y stays as it was."""
+    import torch
+    cases = [synth.get_workload("tiny"), small_bf16(L=2, R=64)]
+    for w in cases:
+        lengths, slots = np.array([3, 2], np.int64), np.array([0, 1], np.int32)
+        stacks = pack_stacks(w, 0, np.full(w.max_num_loras, 4, np.int32))
+        acts = synth.draw_activations(w, 0, 5)
+        gl = GpuLayer(w, stacks, lengths, slots, acts)
+        y0 = gl.dev["y_qkv"].clone()
+        with pytest.raises(srg.LoraError):
+            srg.lora_sgmv_delta(gl.dims, srg.FAMILY_QKV, gl.dev["x_qkv"], gl.st["A_qkv"], gl.st["B_qkv"],
+                                gl.routing["host"], gl.dev["y_qkv"], gl.ws[srg.FAMILY_QKV], srg.PATH_FUSED)
+        torch.cuda.synchronize()
+        assert torch.equal(gl.dev["y_qkv"], y0)
+    w = small_bf16(L=2, R=16)
+    stacks = pack_stacks(w, 0, np.full(2, 4, np.int32))
+    gl = GpuLayer(w, stacks, np.array([3], np.int64), np.array([1], np.int32), synth.draw_activations(w, 0, 3))
+    with pytest.raises(srg.LoraError):
+        srg.lora_sgmv_shrink(gl.dims, srg.FAMILY_QKV, gl.dev["x_qkv"], gl.st["A_qkv"], gl.routing["host"],
+                             gl.u[srg.FAMILY_QKV], gl.ws[srg.FAMILY_QKV], srg.PATH_FUSED)
+    with pytest.raises(srg.LoraError):
+        srg.lora_sgmv_expand(gl.dims, srg.FAMILY_QKV, gl.u[srg.FAMILY_QKV], gl.st["B_qkv"], gl.routing["host"],
+                             gl.dev["y_qkv"], srg.PATH_FUSED)
 
 
 @pytest.mark.parametrize("path", ["auto", "valu"])
