@@ -3,8 +3,10 @@
 
 A step is one batch through the whole hot path: host routing of the batch
 (lora_build_routing), upload of the routing arrays, then for every layer the
-fused-QKV delta (shrink + expand) and the o_proj delta (shrink + expand).
-Adapters are packed (lora_pack_adapter) once, at activation, before timing.
+fused-QKV delta (shrink + expand) and the o_proj delta (shrink + expand), by
+default through lora_sgmv_delta (one call per family; on decode batches that
+is one kernel).  Adapters are packed (lora_pack_adapter) once, at activation,
+before timing.
 
 Default workload: Llama-3-8B attention (hidden 4096, 32 heads, 8 kv heads,
 head_dim 128), 256 one-token decode requests, 8 adapter slots with ranks 8/16
@@ -18,10 +20,17 @@ second (tokens through one layer's q/k/v/o delta per second).
 Phases:
   1. timed steps, the layer loop captured once in a HIP graph and replayed
      (host routing + routing upload stay eager every step);
-  2. the same steps launched eagerly with HIP events around every kernel on
-     the launch stream: per-kernel average duration -> roofline of the
-     dominant kernel;
+  2. per call kind, the call over all layers back to back between two HIP
+     events on the launch stream: average duration per call -> roofline of
+     the dominant call (algorithmic bytes / duration);
   3. the CPU oracle on a bounded sample of the same workload (one core).
+
+Counter runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
+  bench.py --counters delta_qkv [--workload ...]       (GPU, under rocprofv3)
+  bench.py --traffic-from FETCH.csv WRITE.csv --traffic-kind delta_qkv
+writes profiles/traffic.json (HBM bytes per call, calibrated against a plain
+256 MiB copy in the same run), which the roofline line reports as `traffic`
+while the kernel source is unchanged.
 """
 
 import argparse
@@ -49,7 +58,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode", choices=list(REPLICAS))
     p.add_argument("--layers", type=int, default=0, help="override layer replicas per step")
-    p.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "fused"])
     p.add_argument("--api", default="delta", choices=["delta", "split"],
                    help="delta: lora_sgmv_delta per family; split: lora_sgmv_shrink + lora_sgmv_expand")
     p.add_argument("--no-graph", action="store_true")
@@ -57,7 +66,72 @@ def parse():
                    help="kernels read the routing from device memory only (no host copies)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--counters", metavar="KIND", default=None,
+                   help="counter-collection run: a plain copy of COPY_MIB MiB (calibration), then the "
+                        "call KIND (e.g. delta_qkv) over every layer twice; no timing, no JSON line")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="write profiles/traffic.json from the counter_collection.csv files of two "
+                        "--counters runs (FETCH_SIZE, then WRITE_SIZE); needs no GPU")
+    p.add_argument("--traffic-kind", default="delta_qkv")
     return p.parse_args()
+
+
+COPY_MIB = 256
+
+
+def summarize_traffic(args):
+    """HBM bytes per call of one call kind from rocprofv3 --pmc runs.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the library's kernels are
+    scaled by the ratio known bytes / counter value of a plain copy kernel of
+    COPY_MIB MiB measured in the same run; a call of several kernels (split
+    shrink + slab reduction, or the two-kernel delta) adds its kernels."""
+    import csv
+    from collections import defaultdict
+
+    def read(path, counter):
+        lib, copy = defaultdict(list), []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+                if "lora::" in name:
+                    lib[name].append(v)
+                elif "copyBuffer" in name and v * 1024 >= 0.25 * COPY_MIB * 2**20:
+                    copy.append(v)
+        if not copy or not lib:
+            raise SystemExit(f"{path}: no calibration copy or no library kernel with {counter}")
+        return lib, float(np.mean(copy))
+
+    fetch, fetch_copy = read(args.traffic_from[0], "FETCH_SIZE")
+    write, write_copy = read(args.traffic_from[1], "WRITE_SIZE")
+    known = COPY_MIB * 2**20
+    f_fac, w_fac = known / (fetch_copy * 1024), known / (write_copy * 1024)
+    kern = {}
+    total = 0.0
+    for name in sorted(fetch):
+        fk, wk = float(np.mean(fetch[name])), float(np.mean(write.get(name, [0.0])))
+        b = fk * 1024 * f_fac + wk * 1024 * w_fac
+        kern[name] = {"dispatches": len(fetch[name]), "fetch_kib": fk, "write_kib": wk, "hbm_bytes": b}
+        total += b
+    out = {"kernel_sha": kernel_sha(),
+           "copy_calibration": {"bytes": known, "fetch_kib": fetch_copy, "write_kib": write_copy,
+                                "fetch_factor": f_fac, "write_factor": w_fac},
+           "kernels": {f"{args.workload}:{args.traffic_kind}": {"hbm_bytes_per_launch": total,
+                                                                "per_kernel": kern}}}
+    old = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            old = json.load(fh)
+    if old.get("kernel_sha") == out["kernel_sha"]:
+        old.setdefault("kernels", {}).update(out["kernels"])
+        old["copy_calibration"] = out["copy_calibration"]
+        out = old
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out["kernels"]), flush=True)
 
 
 def kernel_sha() -> str:
@@ -67,6 +141,9 @@ def kernel_sha() -> str:
 
 def main():
     args = parse()
+    if args.traffic_from:
+        summarize_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
@@ -81,7 +158,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    path = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA}[args.path]
+    path = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA,
+            "fused": srg.PATH_FUSED}[args.path]
 
     w = synth.get_workload(args.workload)
     n_layers = args.layers or REPLICAS[args.workload]
@@ -165,28 +243,40 @@ def main():
     else:
         KINDS = ("shrink_qkv", "expand_qkv", "shrink_o", "expand_o")
 
-    def layer_pass(ly, events=None):
-        def rec(kind, i):
-            if events is not None:
-                events[kind][i].record()
-        for f, nm, xk, yk, ak, bk in FAMS:
-            if args.api == "delta":
-                rec("delta_" + nm, 0)
-                srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path)
-                rec("delta_" + nm, 1)
-            else:
-                rec("shrink_" + nm, 0)
-                srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], routing, u[f], ws[f], path)
-                rec("shrink_" + nm, 1)
-                rec("expand_" + nm, 0)
-                srg.lora_sgmv_expand(dims, f, u[f], ly[bk], routing, ly[yk], path)
-                rec("expand_" + nm, 1)
+    def call(kind, ly):
+        f, nm, xk, yk, ak, bk = FAMS[0] if kind.endswith("_qkv") else FAMS[1]
+        if kind.startswith("delta"):
+            srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path)
+        elif kind.startswith("shrink"):
+            srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], routing, u[f], ws[f], path)
+        else:
+            srg.lora_sgmv_expand(dims, f, u[f], ly[bk], routing, ly[yk], path)
+
+    def layer_pass(ly):
+        for kind in KINDS:
+            call(kind, ly)
 
     def all_layers():
         for ly in layers:
             layer_pass(ly)
 
     stream = torch.cuda.Stream()
+    if args.counters:
+        # counter-collection run: calibration copy, then only the counted
+        # call, twice per layer (no other call runs in this process)
+        src = torch.ones(COPY_MIB * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            route_and_upload()
+            for _ in range(3):
+                dst.copy_(src)
+            for _ in range(2):
+                for ly in layers:
+                    call(args.counters, ly)
+        torch.cuda.synchronize()
+        log(f"counters: copy {COPY_MIB} MiB x 3, {args.counters} x {2 * n_layers}")
+        return
+
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         route_and_upload()
@@ -220,23 +310,20 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log(f"phase 1: {ms_per_step:.4f} ms/step")
 
-    # ---- phase 2: eager steps with events around every call.  A bounded
-    # spin kernel (torch.cuda._sleep) runs first so that the host has queued
-    # the whole step before the GPU reaches it: the events then time the
-    # kernels back to back, not the host's launch rate.
-    ev_steps = max(1, min(args.steps, 50))
-    pairs = {k: [] for k in KINDS}
+    # ---- phase 2: per-call durations with HIP events on the launch stream.
+    # For every call kind the same call runs over all layers back to back
+    # (cold data, as in the step) between one pair of events; a bounded spin
+    # kernel (torch.cuda._sleep) runs first so that the host has queued the
+    # whole sequence before the GPU reaches it, so the events time the
+    # kernels and not the host's launch rate.
+    ev_reps = max(1, min(args.steps, 20))
+    total_ms = {k: 0.0 for k in KINDS}
     with torch.cuda.stream(stream):
-        for _ in range(2):
-            route_and_upload()
-            all_layers()
-        torch.cuda.synchronize()
-        # host time to enqueue one instrumented step, and the spin rate
-        t0 = time.perf_counter()
         route_and_upload()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for ly in layers:
-            layer_pass(ly, {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                            for k in KINDS})
+            call(KINDS[0], ly)
         enqueue_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,18 +332,18 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         s_per_cycle = max(e0.elapsed_time(e1) * 1e-3 / 1e6, 1e-12)
-        spin = int(min(2.0 * enqueue_s / s_per_cycle, 2e10))
-        for _ in range(ev_steps):
-            torch.cuda._sleep(spin)
-            route_and_upload()
-            for ly in layers:
-                ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for k in KINDS}
-                layer_pass(ly, ev)
-                for k in KINDS:
-                    pairs[k].append(ev[k])
-            torch.cuda.synchronize()
-    avg_us = {k: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in pairs[k]])) for k in KINDS}
+        spin = int(min(3.0 * enqueue_s / s_per_cycle + 1e5, 2e10))
+        for _ in range(ev_reps):
+            for kind in KINDS:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(spin)
+                a.record()
+                for ly in layers:
+                    call(kind, ly)
+                b.record()
+                torch.cuda.synchronize()
+                total_ms[kind] += a.elapsed_time(b)
+    avg_us = {k: 1e3 * total_ms[k] / (ev_reps * n_layers) for k in KINDS}
     log("phase 2: " + " ".join(f"{k}={v:.2f}us" for k, v in avg_us.items()))
 
     # algorithmic bytes per call (u, the rank-space intermediate, counted for
@@ -292,33 +379,38 @@ def main():
     value = end * n_layers / (ms_per_step * 1e-3)
     e2e_gbs = fam_bytes * n_layers / (ms_per_step * 1e-3) / 1e9
 
-    # ---- phase 3: CPU oracle on a bounded sample
+    # ---- phase 3: CPU oracle on a bounded sample: whole layers (both
+    # families) of the same workload, cycling over a few distinct layers and
+    # rotating which requests a layer's row budget covers, until about
+    # --cpu-seconds of oracle time has been spent
     cpu = None
     if not args.no_cpu:
         import oracle
-        tokens_done = 0
-        t_cpu = 0.0
-        sample_layers = 0
-        for l in range(n_layers):
-            st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
-            for s in range(L):
-                pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
-                                         int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
-                                         synth.draw_adapter(w, l, s, int(ranks[s])))
-                for k in st:
-                    st[k].append(pk[k])
-            st = {k: np.stack(v) for k, v in st.items()}
-            acts = synth.draw_activations(w, l, T)
-            lora_req = [i for i in range(len(slots)) if slots[i] >= 0]
-            # bound the work per layer for the long workloads
-            budget = max(1, int(2e8 // (fam_shape[0][0] * fam_shape[0][1] * R + fam_shape[0][3] * R)))
-            rows = {}
-            left = budget
-            for i in lora_req:
+        tokens_done, t_cpu, n_calls = 0, 0.0, 0
+        prepared = []
+        n_distinct = min(n_layers, 4)
+        lora_req = [i for i in range(len(slots)) if slots[i] >= 0]
+        # bound the rows per call for the long workloads (about 0.1-1 s each)
+        budget = max(1, int(2e8 // (fam_shape[0][0] * fam_shape[0][1] * R + fam_shape[0][3] * R)))
+        while t_cpu < args.cpu_seconds and n_calls < 100000:
+            l = n_calls % n_distinct
+            if l >= len(prepared):
+                st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+                for s in range(L):
+                    pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
+                                             int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
+                                             synth.draw_adapter(w, l, s, int(ranks[s])))
+                    for k in st:
+                        st[k].append(pk[k])
+                prepared.append(({k: np.stack(v) for k, v in st.items()}, synth.draw_activations(w, l, T)))
+            st, acts = prepared[l]
+            order_req = lora_req[n_calls % len(lora_req):] + lora_req[:n_calls % len(lora_req)]
+            rows, left = {}, budget
+            for i in order_req:
                 n = int(lengths[i])
                 rows[i] = np.arange(min(n, max(left, 0)))
                 left -= len(rows[i])
-            reqs = [i for i in lora_req if len(rows[i])]
+            reqs = [i for i in order_req if len(rows[i])]
             t0 = time.perf_counter()
             oracle.reference_family(acts["x_qkv"], acts["y_qkv"], offsets, slots, st["A_qkv"], st["B_qkv"],
                                     [w.nq, w.nkv, w.nkv], R, w.dtype, reqs, rows)
@@ -326,13 +418,12 @@ def main():
                                     [w.hidden], R, w.dtype, reqs, rows)
             t_cpu += time.perf_counter() - t0
             tokens_done += sum(len(rows[i]) for i in reqs)
-            sample_layers += 1
-            if t_cpu >= args.cpu_seconds:
-                break
+            n_calls += 1
         cpu = {"value": tokens_done / t_cpu, "unit": "LoRA tokens x layers / s", "cores": 1,
                "kind": "oracle",
-               "sample": f"{tokens_done} LoRA-routed token rows over {sample_layers} layer(s) of the same "
-                         f"workload (q/k/v/o delta, fp64, single thread), {t_cpu:.1f} s"}
+               "sample": f"{tokens_done} LoRA-routed token rows through the q/k/v/o delta of one layer "
+                         f"({n_calls} oracle passes over {len(prepared)} distinct layers of the same "
+                         f"workload, at most {budget} rows per pass), fp64, single thread, {t_cpu:.1f} s"}
         log(f"phase 3: oracle {cpu['value']:.1f} tokens x layers/s")
 
     out = {
