@@ -646,11 +646,139 @@ __device__ __forceinline__ void stage_u(const ExpandArgs& a, const TileInfo& ti,
 // (features) and u the N operand (tokens).  The M rows of block h of pair p
 // are permuted to features 32p + 8(i/4) + 4h + i%4, so that lane (token j,
 // group q) holds features 32p + 8q .. 32p + 8q + 7 across the two
+// accumulators, and y is the C operand.
+//
+// y moves through LDS: the workgroup loads its [64 x ft] tile of y with
+// coalesced 16-byte runs (every row segment a whole number of 128-byte
+// lines), the waves read their MFMA C operands from LDS and write the
+// results back in place, and the tile is stored with the same coalesced
+// runs.  Reading y in the MFMA layout directly would split every line over
+// two instructions (16 rows x 64 bytes each) and double the line requests.
+// y and (for NH == 1) B fragments are loaded before u is staged.
+constexpr int kYLd = kExpandCols + 8;  // padded LDS row of the y tile (bf16 elements)
+
+template <int NH>
+__device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
+                                            const Buf& yb, int ucol0, float* us, float4* part,
+                                            uint16_t* ylds)
+{
+    constexpr int kMaxPairs = kExpandCols / 32;
+    constexpr bool kPrefetchB = NH == 1;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int np = a.ft >> 5;
+    const int pieces = a.ft >> 3;  // 16-byte pieces per row of the tile
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0
+    const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * a.R;
+
+    // coalesced y tile: 64 rows x `pieces` pieces, kMaxPairs rounds of 256 pieces
+    uint4 yraw[kMaxPairs];
+#pragma unroll
+    for (int i = 0; i < kMaxPairs; ++i) {
+        const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
+        yraw[i] = yb.ld16(i < np ? (uint32_t)(row * a.ldy + f0 + 8 * pc) * 2 : kOOB);
+    }
+    uint4 bfr[kPrefetchB ? kMaxPairs : 1][2][NH];
+    if constexpr (kPrefetchB) {
+#pragma unroll
+        for (int p = 0; p < kMaxPairs; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kh = 0; kh < NH; ++kh)
+                    bfr[p][h][kh] = ld16(Bb + (size_t)(min(p, np - 1) * 32 + mrow + 4 * h) * a.R + 16 * kh +
+                                         8 * (q & 1));
+    }
+    // u first: its loads go out before the wait on y
+    stage_u(a, ti, ucol0, us, part);
+#pragma unroll
+    for (int i = 0; i < kMaxPairs; ++i) {
+        if (i < np) {
+            const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
+            *reinterpret_cast<uint4*>(ylds + row * kYLd + 8 * pc) = yraw[i];
+        }
+    }
+    __syncthreads();
+
+    if (16 * w < ti.n) {
+        // u fragments: lanes q<2 carry hi(u[t][16kh+8q..]), lanes q>=2 lo(u[t][16kh+8(q-2)..])
+        const int t = 16 * w + l16;
+        bf16x8_t uf[NH];
+#pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+            const float* up = us + min(t, ti.n - 1) * a.R + 16 * kh + 8 * (q & 1);
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v0 = up[2 * e], v1 = up[2 * e + 1];
+                uint32_t hi = f2bf_pair(v0, v1);
+                if (q >= 2)
+                    hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+                pk[e] = hi;
+            }
+            uf[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+
+#pragma unroll
+        for (int p = 0; p < kMaxPairs; ++p) {
+            if (p < np) {
+                uint4* cell = reinterpret_cast<uint4*>(ylds + t * kYLd + 32 * p + 8 * q);
+                const uint4 yv = *cell;
+                f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
+                f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+#pragma unroll
+                for (int kh = 0; kh < NH; ++kh) {
+                    uint4 b0, b1;
+                    if constexpr (kPrefetchB) {
+                        b0 = bfr[p][0][kh];
+                        b1 = bfr[p][1][kh];
+                    } else {
+                        const uint16_t* bp = Bb + (size_t)(p * 32 + mrow) * a.R + 16 * kh + 8 * (q & 1);
+                        b0 = ld16(bp);
+                        b1 = ld16(bp + 4 * a.R);
+                    }
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[kh], acc0,
+                                                                  0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[kh], acc1,
+                                                                  0, 0, 0);
+                }
+                uint4 o;
+                o.x = f2bf_pair(acc0[0], acc0[1]);
+                o.y = f2bf_pair(acc0[2], acc0[3]);
+                o.z = f2bf_pair(acc1[0], acc1[1]);
+                o.w = f2bf_pair(acc1[2], acc1[3]);
+                *cell = o;
+            }
+        }
+    }
+    __syncthreads();
+    // rows past the tile's tokens drop their stores (offset past the resource)
+#pragma unroll
+    for (int i = 0; i < kMaxPairs; ++i) {
+        if (i < np) {
+            const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
+            yb.st16((uint32_t)(row * a.ldy + f0 + 8 * pc) * 2,
+                    *reinterpret_cast<const uint4*>(ylds + row * kYLd + 8 * pc));
+        }
+    }
+}
+
+// MFMA path with y in registers (ranks 32 and 64, whose B fragments do not
+// fit a register prefetch).  Wave w owns tokens 16w .. 16w+15 of the tile and walks
+// the feature tile in pairs of 16-feature MFMA blocks.  For each 16 ranks one
+// v_mfma_f32_16x16x32_bf16 per block computes B·u with K = 32 = 16 ranks of
+// the high bf16 half of u followed by the same 16 ranks of its low half
+// (u = hi + lo to ~2^-17 relative), so u keeps fp32 precision while the
+// products run on the bf16 matrix cores.  B rows are the M operand
+// (features) and u the N operand (tokens).  The M rows of block h of pair p
+// are permuted to features 32p + 8(i/4) + 4h + i%4, so that lane (token j,
+// group q) holds features 32p + 8q .. 32p + 8q + 7 across the two
 // accumulators: y is the C operand, read and written as 16-byte runs in the
 // MFMA layout itself, and a wave covers 16 rows x 512 contiguous bytes.
 // y and (for NH <= 2) B fragments are loaded before u is staged.
 template <int NH>
-__device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
+__device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileInfo& ti, int f0,
                                             const Buf& yb, int ucol0, float* us, float4* part)
 {
     constexpr int kMaxPairs = kExpandCols / 32;
@@ -820,6 +948,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     extern __shared__ float smem[];
     float* us = smem;                                             // [kTileM][R]
     float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads]
+    uint16_t* ylds = reinterpret_cast<uint16_t*>(part + kThreads);  // [kTileM][kYLd] (MFMA path)
 
     const int lin = blockIdx.x;
     const int ftile = lin % a.n_ftiles;
@@ -831,11 +960,17 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     const int ucol0 = slice_of(a, f0) * a.R;
     const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
     if constexpr (NH > 0 && MODE == kMfmaOnly) {
-        expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part);
-    } else if constexpr (NH > 0 && MODE == kMixed) {
-        if (ti.glen > a.valu_max)
-            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part);
+        if constexpr (NH == 1)
+            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
         else
+            expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
+    } else if constexpr (NH > 0 && MODE == kMixed) {
+        if (ti.glen > a.valu_max) {
+            if constexpr (NH == 1)
+                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
+            else
+                expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
+        } else
             expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
     } else {
         expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
@@ -1193,9 +1328,10 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     const int64_t grid = tiles * a.n_ftiles;
     if (grid > 2147483647LL)
         return LORA_ERR_INVALID_ARGUMENT;
-    const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4);
-    const dim3 g((unsigned)grid), b(kThreads);
     const int nh = nh_possible(c, a) ? c.fs.R / 16 : 0;
+    const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4) +
+                       (nh == 1 ? (size_t)kTileM * kYLd * sizeof(uint16_t) : 0);
+    const dim3 g((unsigned)grid), b(kThreads);
     const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
 #define LORA_EXPAND_NH(NHV)                                                                       \
     if (mode == kMfmaOnly)                                                                        \
