@@ -106,8 +106,18 @@ const char* lora_status_string(lora_status_t status);
 
 /* Shape of a projection family: input width, slice count (1..4), the slice
  * widths (slice_widths needs room for 4 entries) and the total output width.
- * The packed stacks of the family are A [L][n_slices*R][in_features] and
- * B [L][out_features][R]. */
+ * The packed stacks of the family are A [L][rows_t][in_features] in the
+ * tiled layout below and B [L][out_features][R] row-major.
+ *
+ * A layout.  Logically A of one slot is [n_slices*R][in_features] (the rank
+ * rows of q, k, v stacked, [MAX-lora] QKV 融合).  On the device the rows are
+ * grouped in blocks of 16 (rows_t = n_slices*R rounded up to 16; the rows
+ * added are zero) and each block is stored as 8-element pieces along K,
+ * piece-major then row:
+ *   A[row][k]  at element  ((row/16) * (K/8) + k/8) * 128 + (row%16) * 8 + k%8
+ * with K = in_features.  This puts the 16 rows x 32 K values that one matrix
+ * instruction consumes in one contiguous 1 KB run.  A slot holds
+ * rows_t * in_features elements. */
 lora_status_t lora_family_shape(const lora_dims_t* dims, int32_t family, int32_t* in_features,
                                 int32_t* n_slices, int32_t* slice_widths, int32_t* out_features);
 
@@ -131,9 +141,11 @@ lora_status_t lora_family_shape(const lora_dims_t* dims, int32_t family, int32_t
  * targeted projections (NULL allowed for the others); in_q = in_k = in_v =
  * hidden, in_o = n_heads*head_dim; out_q = n_heads*head_dim, out_k = out_v =
  * n_kv_heads*head_dim, out_o = hidden.
- * Outputs (host memory, dims->dtype): A_qkv [3R][hidden],
- * B_qkv [nq+2nkv][R], A_o [R][nq], B_o [hidden][R] — one slot each; the
- * caller copies them into slot s of the device stacks.
+ * Outputs (host memory, dims->dtype): A_qkv [3R][hidden] and A_o [R][nq] in
+ * the tiled A layout (see lora_family_shape: round16(3R) * hidden and
+ * round16(R) * nq elements), B_qkv [nq+2nkv][R] and B_o [hidden][R]
+ * row-major — one slot each; the caller copies them into slot s of the
+ * device stacks.
  */
 lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lora_alpha,
                                 int32_t use_rslora, int32_t bias_none, uint32_t target_mask,
@@ -224,7 +236,8 @@ typedef struct lora_routing {
  *
  * x        [>= end rows][in_features] in dims->dtype, row stride ldx elements;
  *          rows >= end are not read.
- * A_stack  [L][n_slices*R][in_features] in dims->dtype (the family's packed stack).
+ * A_stack  [L][round16(n_slices*R)][in_features] in dims->dtype, tiled layout
+ *          (see lora_family_shape; lora_pack_adapter writes it).
  * routing  see lora_routing_t.
  * u        fp32 [end][n_slices*R] (device).
  * workspace: device scratch, >= lora_sgmv_workspace_bytes(dims, family, end)

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     LoraDims,
     LoraRouting,
     LoraError,
+    a_tiled_shape,
     family_shape,
     library_path,
     lora_abi_version,
@@ -34,4 +35,6 @@ from ._lib import (  # noqa: F401
     lora_sgmv_workspace_bytes,
     lora_status_string,
     packed_to_torch,
+    tile_a,
+    untile_a,
 )

@@ -187,17 +187,44 @@ def lora_family_shape(dims: LoraDims, family: int) -> Tuple[int, int, Tuple[int,
 family_shape = lora_family_shape
 
 
+def a_tiled_shape(rows: int, K: int) -> Tuple[int, int, int, int]:
+    """Shape [blocks, K/8, 16, 8] of one slot of an A stack in the device
+    layout (rows rounded up to a multiple of 16)."""
+    return ((rows + 15) // 16, K // 8, 16, 8)
+
+
+def untile_a(a: np.ndarray, rows: int) -> np.ndarray:
+    """Device-layout A slot(s) [..., blocks, K/8, 16, 8] -> logical
+    [..., rows, K] (drops the zero rows added up to a multiple of 16)."""
+    nb, p = a.shape[-4], a.shape[-3]
+    lead = a.shape[:-4]
+    m = np.swapaxes(a, -3, -2).reshape(*lead, nb * 16, p * 8)
+    return m[..., :rows, :]
+
+
+def tile_a(a: np.ndarray) -> np.ndarray:
+    """Logical A [..., rows, K] -> device layout [..., blocks, K/8, 16, 8]."""
+    rows, K = a.shape[-2], a.shape[-1]
+    nb = (rows + 15) // 16
+    lead = a.shape[:-2]
+    pad = np.zeros((*lead, nb * 16, K), a.dtype)
+    pad[..., :rows, :] = a
+    return np.ascontiguousarray(np.swapaxes(pad.reshape(*lead, nb, 16, K // 8, 8), -3, -2))
+
+
 def lora_pack_adapter(dims: LoraDims, rank: int, lora_alpha: float, use_rslora: bool,
                       bias_none: bool, targets: Sequence[str],
                       weights: Dict[str, Tuple[np.ndarray, np.ndarray]],
                       target_mask: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Pack one adapter of one layer; returns host arrays A_qkv, B_qkv, A_o,
-    B_o (uint16 bf16 patterns or float32)."""
+    B_o (uint16 bf16 patterns or float32).  A_qkv and A_o come in the device's
+    tiled layout (a_tiled_shape; untile_a gives the logical [rows, K])."""
     R = dims.max_lora_rank
     nq, nkv = dims.n_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
     st = np.uint16 if dims.dtype == "bf16" else np.float32
-    out = {"A_qkv": np.empty((3 * R, dims.hidden), st), "B_qkv": np.empty((nq + 2 * nkv, R), st),
-           "A_o": np.empty((R, nq), st), "B_o": np.empty((dims.hidden, R), st)}
+    out = {"A_qkv": np.empty(a_tiled_shape(3 * R, dims.hidden), st),
+           "B_qkv": np.empty((nq + 2 * nkv, R), st),
+           "A_o": np.empty(a_tiled_shape(R, nq), st), "B_o": np.empty((dims.hidden, R), st)}
     if target_mask is None:
         target_mask = 0
         for t in targets:

@@ -234,17 +234,27 @@ lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lor
     const float scale32 = (float)scale;
     const bool bf16 = dims->dtype == LORA_DTYPE_BF16;
 
+    // A tensors are written in the tiled device layout (a_tiled_index); rows
+    // of the last 16-row block past n_slices*R are zero
+    if (bf16) {
+        memset(A_qkv_out, 0, (size_t)a_tiled_elems(3 * R, H) * 2);
+        memset(A_o_out, 0, (size_t)a_tiled_elems(R, nq) * 2);
+    } else {
+        memset(A_qkv_out, 0, (size_t)a_tiled_elems(3 * R, H) * 4);
+        memset(A_o_out, 0, (size_t)a_tiled_elems(R, nq) * 4);
+    }
     for (int p = 0; p < 4; ++p) {
         const bool on = (target_mask >> p) & 1u;
         // A block: rows [a_row0, a_row0 + R) of width in_p; rows >= rank are zero
         for (int64_t i = 0; i < R; ++i) {
             const int64_t row = a_row0[p] + i;
             for (int64_t k = 0; k < in_p[p]; ++k) {
-                float v = (on && i < r) ? A_in[p][i * in_p[p] + k] : 0.0f;
+                const float v = (on && i < r) ? A_in[p][i * in_p[p] + k] : 0.0f;
+                const int64_t at = a_tiled_index(row, k, in_p[p]);
                 if (bf16)
-                    ((uint16_t*)A_dst[p])[row * in_p[p] + k] = to_bf16(v);
+                    ((uint16_t*)A_dst[p])[at] = to_bf16(v);
                 else
-                    ((float*)A_dst[p])[row * in_p[p] + k] = v;
+                    ((float*)A_dst[p])[at] = v;
             }
         }
         // B block: rows [b_row0, b_row0 + out_p) of width R; columns >= rank are zero

@@ -42,6 +42,19 @@ struct FamilyShape {
     int elem;        // bytes per element of x / y / stacks
 };
 
+// Device layout of an A stack slot (rows = the n_slices*R rank rows, K = the
+// input width, a multiple of 8): the rows in blocks of 16; inside a block,
+// 8-element pieces along K are stored piece-major, then row:
+//   A[row][k] -> ((row / 16) * (K / 8) + k / 8) * 128 + (row % 16) * 8 + k % 8.
+// One MFMA operand load (lane = 16 * k-group + row, 16 bytes each) of a
+// 32-element K step is then one contiguous 1 KB run.
+inline int64_t a_tiled_rows(int64_t rows) { return (rows + 15) / 16 * 16; }
+inline int64_t a_tiled_elems(int64_t rows, int64_t K) { return a_tiled_rows(rows) * K; }
+inline int64_t a_tiled_index(int64_t row, int64_t k, int64_t K)
+{
+    return ((row / 16) * (K / 8) + k / 8) * 128 + (row % 16) * 8 + k % 8;
+}
+
 lora_status_t check_dims(const lora_dims_t* d);
 lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs);
 

@@ -283,7 +283,8 @@ __device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
 struct ShrinkArgs {
     const void* x;
     int64_t ldx;
-    const void* A;  // [L][C][in_f]
+    const void* A;  // [L][a_slot] in the tiled A layout (a_tiled_index)
+    int64_t a_slot;  // elements per slot: C rounded up to 16, times in_f
     float* out;     // slab s at out + s * slab, each [end][C]; S == 1: u itself
     int64_t slab;
     int in_f, C;
@@ -292,73 +293,81 @@ struct ShrinkArgs {
     RouteArgs r;
 };
 
-// VALU path (decode-shaped tiles, and every fp32 tile).  A wave is four
-// 16-lane groups; each group owns one output column at a time and its lanes
-// walk K in 8-element runs (128 elements per pass), so a 16-lane wavefront
-// reduction finishes every (token, column) dot product.  Columns are taken
-// four per group per pass (16 per wave, 64 per workgroup) and tokens eight at
-// a time: 12 independent 16-byte loads per pass.  Rows past the tile and
-// columns past the group read as zero through the buffer resources.
+// VALU path (decode-shaped tiles, and every fp32 tile).  The columns
+// [c0, c1) are nbk <= 4 blocks of 16 A rows; the four waves take one block
+// each (nbk >= 3) or split the K range 4 / nbk ways per block.  Lane
+// (g = lane / 16, r = lane % 16) owns column 16 b + r and the K pieces
+// g, g + 4, g + 8, ... of its wave's range, so the four 16-lane groups read
+// four consecutive pieces of the tiled A: one contiguous run per load.  The
+// x piece of a token is the same for the 16 lanes of a group.  Tokens go
+// eight at a time; two xor steps over lane bits 4 and 5 add the four K
+// groups, and the K-split waves are added in wave order through LDS
+// (res: [4][kTileM][16 nbk] fp32).  Rows past the tile read as zero.
 template <typename T>
 __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int k1, int c0,
-                            int c1, float* res, int res_ld)
+                            int c1, float* dst, int64_t dst_ld, float* res)
 {
     constexpr int E = sizeof(T);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int g16 = lane >> 4, l16 = lane & 15;
-    const int slot_col = 4 * w + g16;  // 0..15
+    const int g = lane >> 4, r = lane & 15;
+    const int cw = c1 - c0, nbk = (cw + 15) >> 4;
+    const int kparts = 4 / nbk;
+    const int b = w % nbk, kp = w / nbk;
+    const int ldr = 16 * nbk;
+    // pieces (8 elements) of the workgroup's K range, split over kparts waves
+    const int pw0 = k0 >> 3, pw1 = (k1 + 7) >> 3;
+    const int per = (pw1 - pw0 + kparts - 1) / kparts;
+    const int q0 = pw0 + kp * per, q1 = min(q0 + per, pw1);
     const T* X = reinterpret_cast<const T*>(a.x) + (size_t)ti.t0 * a.ldx;
-    const T* Ab = reinterpret_cast<const T*>(a.A) + ((size_t)ti.slot * a.C + c0) * a.in_f;
+    const T* Ab = reinterpret_cast<const T*>(a.A) + (size_t)ti.slot * a.a_slot + (size_t)((c0 >> 4) + b) * 16 * a.in_f;
     const Buf xb(X, (uint32_t)(ti.n * a.ldx * E));
-    const Buf ab(Ab, (uint32_t)((c1 - c0) * a.in_f * E));
+    const Buf ab(Ab, (uint32_t)(16 * a.in_f * E));
+    const bool active = kp < kparts;  // with three blocks the fourth wave idles
     for (int tb = 0; tb < ti.n; tb += 8) {
-        const int nt = min(8, ti.n - tb);
-        for (int cb = 0; cb < c1 - c0; cb += 64) {
-            float acc[4][8];
+        float acc[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[j][i] = 0.f;
-            for (int k = k0 + 8 * l16; k < k1; k += 128) {
-                float av[4][8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t off = (uint32_t)((cb + slot_col + 16 * j) * a.in_f + k) * E;
-                    Vec8<T>::unpack(Vec8<T>::load_raw(ab, off), av[j]);
-                }
-                typename Vec8<T>::Raw xr[8];  // rows past the tile read as zero
+        for (int i = 0; i < 8; ++i)
+            acc[i] = 0.f;
+        if (active) {
+#pragma unroll 2
+            for (int p = q0 + g; p < q1; p += 4) {
+                float av[8];
+                Vec8<T>::unpack(Vec8<T>::load_raw(ab, (uint32_t)((p * 16 + r) * 8) * E), av);
+                typename Vec8<T>::Raw xr[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    xr[i] = Vec8<T>::load_raw(xb, (uint32_t)((tb + i) * a.ldx + k) * E);
+                    xr[i] = Vec8<T>::load_raw(xb, (uint32_t)((tb + i) * a.ldx + 8 * p) * E);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    if (i < nt) {
-                        float xv[8];
-                        Vec8<T>::unpack(xr[i], xv);
+                    float xv[8];
+                    Vec8<T>::unpack(xr[i], xv);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                acc[j][i] = fmaf(av[j][e], xv[e], acc[j][i]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = cb + slot_col + 16 * j;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float v = acc[j][i];
-                    v += __shfl_xor(v, 8, 64);
-                    v += __shfl_xor(v, 4, 64);
-                    v += __shfl_xor(v, 2, 64);
-                    v += __shfl_xor(v, 1, 64);
-                    if (l16 == 0 && i < nt && c < c1 - c0)
-                        res[(tb + i) * res_ld + c] = v;
+                    for (int e = 0; e < 8; ++e)
+                        acc[i] = fmaf(av[e], xv[e], acc[i]);
                 }
             }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = acc[i];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[i] = v;
+        }
+        if (active && g == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (tb + i < ti.n)
+                    res[(kp * kTileM + tb + i) * ldr + 16 * b + r] = acc[i];
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < ti.n * cw; e += kThreads) {
+        const int t = e / cw, c = e - t * cw;
+        float v = res[t * ldr + c];
+        for (int k = 1; k < kparts; ++k)
+            v += res[(k * kTileM + t) * ldr + c];
+        dst[(size_t)t * dst_ld + c] = v;
     }
 }
 
@@ -394,9 +403,11 @@ __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int
     uint16_t* lx = lds;
     uint16_t* la = lds + Lay::kX;
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x) + (size_t)ti.t0 * a.ldx;
-    const uint16_t* Ab = reinterpret_cast<const uint16_t*>(a.A) + ((size_t)ti.slot * a.C + c0) * a.in_f;
-    const Buf xb(X, (uint32_t)(ti.n * a.ldx * 2));             // rows past the tile read as zero
-    const Buf ab(Ab, (uint32_t)((c1 - c0) * a.in_f * 2));      // columns past the group read as zero
+    // the group's A blocks in the tiled layout; blocks past the group read as zero
+    const uint16_t* Ab =
+        reinterpret_cast<const uint16_t*>(a.A) + (size_t)ti.slot * a.a_slot + (size_t)(c0 >> 4) * 16 * a.in_f;
+    const Buf xb(X, (uint32_t)(ti.n * a.ldx * 2));  // rows past the tile read as zero
+    const Buf ab(Ab, (uint32_t)(((c1 - c0 + 15) >> 4) * 16 * a.in_f * 2));
     const int nchunks = (k1 - k0 + KC - 1) / KC;
 
     uint4 xs[XR], as[AR];
@@ -407,10 +418,15 @@ __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int
             const int p = tid + kThreads * i, r = p / PIECES, k = kb + 8 * (p % PIECES);
             xs[i] = xb.ld16(k < k1 ? (uint32_t)(r * a.ldx + k) * 2 : kOOB);
         }
+        // A piece p: row p % 16 of block p / (16 PIECES), K piece (p / 16) % PIECES;
+        // 16 consecutive threads read one contiguous 256-byte piece group
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
-            const int p = tid + kThreads * i, r = p / PIECES, k = kb + 8 * (p % PIECES);
-            as[i] = ab.ld16((p < APieces && k < k1) ? (uint32_t)(r * a.in_f + k) * 2 : kOOB);
+            const int p = tid + kThreads * i, rr = p & 15, pc = (p >> 4) % PIECES, nb = p / (16 * PIECES);
+            const int k = kb + 8 * pc;
+            as[i] = ab.ld16((p < APieces && k < k1)
+                                ? (uint32_t)(((nb * (a.in_f >> 3) + (k >> 3)) * 16 + rr) * 8) * 2
+                                : kOOB);
         }
     };
     auto lstore = [&]() {
@@ -421,9 +437,9 @@ __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int
         }
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
-            const int p = tid + kThreads * i;
+            const int p = tid + kThreads * i, rr = p & 15, pc = (p >> 4) % PIECES, nb = p / (16 * PIECES);
             if (p < APieces)
-                *reinterpret_cast<uint4*>(la + (p / PIECES) * Lay::kLd + 8 * (p % PIECES)) = as[i];
+                *reinterpret_cast<uint4*>(la + (nb * 16 + rr) * Lay::kLd + 8 * pc) = as[i];
         }
     };
 
@@ -491,9 +507,10 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
     constexpr int KC = kShrinkKC;
     constexpr bool kHasValu = MODE != kValuOnly ? MODE == kMixed : true;
     constexpr bool kHasMfma = MODE != kValuOnly;
-    constexpr int kLdsBytes = (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0) > (kHasValu ? kTileM * CB * 4 : 0)
+    constexpr int kValuLds = 4 * kTileM * 16 * 4;  // shrink_valu's res
+    constexpr int kLdsBytes = (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0) > (kHasValu ? kValuLds : 0)
                                   ? (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0)
-                                  : (kHasValu ? kTileM * CB * 4 : 0);
+                                  : (kHasValu ? kValuLds : 0);
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes > 0 ? kLdsBytes : 16];
 
     const int lin = blockIdx.x;
@@ -518,15 +535,8 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
             return;
         }
     }
-    if constexpr (kHasValu) {
-        float* res = reinterpret_cast<float*>(smem);
-        shrink_valu<T>(a, ti, k0, k1, c0, c1, res, CB);
-        __syncthreads();
-        for (int e = threadIdx.x; e < ti.n * cw; e += kThreads) {
-            const int i = e / cw, c = e - i * cw;
-            dst[(size_t)i * a.C + c] = res[i * CB + c];
-        }
-    }
+    if constexpr (kHasValu)
+        shrink_valu<T>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<float*>(smem));
 }
 
 // u = sum of the S slabs, in split order; 4 floats per thread.
@@ -1003,7 +1013,8 @@ constexpr int kXcds = 8;
 struct FusedArgs {
     const uint16_t* x;
     int64_t ldx;
-    const uint16_t* A;  // [L][C][in_f]
+    const uint16_t* A;  // [L][a_slot] in the tiled A layout (a_tiled_index)
+    int64_t a_slot;     // elements per slot
     const uint16_t* B;  // [L][out_f][R]
     uint16_t* y;
     int64_t ldy;
@@ -1061,10 +1072,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     // --- u partial over the wave's K range: x rows as M, A rows as N.  K
     // positions past the wave's range read as zero (offset kOOB).
     const Buf xb(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));  // rows >= n read zero
-    const Buf ab(a.A + ((size_t)ti.slot * a.C + sl * R) * a.in_f, (uint32_t)(R * a.in_f * 2));
+    // the slice's NH blocks of the tiled A: one step of one block is a 1 KB run
+    const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)sl * R * a.in_f, (uint32_t)(R * a.in_f * 2));
     const int kw0 = w * a.wave_steps * 32;
     const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
-    const uint32_t xrow = (uint32_t)(l16 * a.ldx) * 2, arow = (uint32_t)(l16 * a.in_f) * 2;
+    const uint32_t xrow = (uint32_t)(l16 * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
     f32x4_t acc[NH];
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb)
@@ -1075,11 +1087,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
             const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
-            const uint32_t ko = kk < kw1 ? (uint32_t)kk * 2 : kOOB;
-            xr[i] = xb.ld16(xrow + ko);
+            const bool ok = kk < kw1;
+            xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
+            // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
+            const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
 #pragma unroll
             for (int nb = 0; nb < NH; ++nb)
-                ar[i][nb] = ab.ld16(arow + (uint32_t)(nb * 16 * a.in_f) * 2 + ko);
+                ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
         }
         // keep every load of the batch ahead of the first MFMA: one round trip
         __builtin_amdgcn_sched_barrier(0);
@@ -1284,6 +1298,7 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
     a.x = x;
     a.ldx = ldx;
     a.A = A_stack;
+    a.a_slot = a_tiled_elems(c.fs.C, c.fs.in_f);
     a.out = out;
     a.slab = (int64_t)c.r.end * c.fs.C;
     a.in_f = c.fs.in_f;
@@ -1386,6 +1401,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     a.x = reinterpret_cast<const uint16_t*>(x);
     a.ldx = ldx;
     a.A = reinterpret_cast<const uint16_t*>(A_stack);
+    a.a_slot = a_tiled_elems(c.fs.C, c.fs.in_f);
     a.B = reinterpret_cast<const uint16_t*>(B_stack);
     a.y = reinterpret_cast<uint16_t*>(y);
     a.ldy = ldy;

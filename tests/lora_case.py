@@ -44,17 +44,25 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 def pack_stacks(w: synth.Workload, layer: int, ranks: np.ndarray, targets="qkvo",
                 zero_B: bool = False) -> Dict[str, np.ndarray]:
-    """Stacks [L, ...] of one layer packed by the product library."""
+    """Stacks [L, ...] of one layer: A_qkv / B_qkv / A_o / B_o packed by the
+    product library (device layout, for the GPU) and, under "ref", the same
+    adapters packed by the oracle (logical layout, for the reference)."""
     d = dims_of(w)
     out = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+    ref = {k: [] for k in out}
     for s in range(w.max_num_loras):
         weights = synth.draw_adapter(w, layer, s, int(ranks[s]))
         if zero_B:
             weights = {p: (a, np.zeros_like(b)) for p, (a, b) in weights.items()}
         pk = srg.lora_pack_adapter(d, int(ranks[s]), w.lora_alpha, w.use_rslora, True, targets, weights)
+        po = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank, w.dtype,
+                                 int(ranks[s]), w.lora_alpha, w.use_rslora, True, targets, weights)
         for k in out:
             out[k].append(pk[k])
-    return {k: np.stack(v) for k, v in out.items()}
+            ref[k].append(po[k])
+    stacks = {k: np.stack(v) for k, v in out.items()}
+    stacks["ref"] = {k: np.stack(v) for k, v in ref.items()}
+    return stacks
 
 
 def to_dev(a: np.ndarray, dtype: str):
@@ -96,7 +104,7 @@ class GpuLayer:
         self.T = int(self.offs[-1])
         self.end = self.rt["end"]
         self.G = self.rt["num_groups"]
-        self.st = {k: to_dev(v, w.dtype) for k, v in stacks.items()}
+        self.st = {k: to_dev(v, w.dtype) for k, v in stacks.items() if k != "ref"}
         # routing with host copies (kernel-argument routing) and device-only
         self.routing = {"host": srg.LoraRouting.from_host(self.rt, host_copy=True),
                         "device": srg.LoraRouting.from_host(self.rt, host_copy=False)}
@@ -161,12 +169,13 @@ def oracle_layer(w: synth.Workload, stacks: Dict[str, np.ndarray], lengths, slot
     """Oracle reference of both families: {family: {request: (rows, y_ref, u)}}."""
     offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     R = w.max_lora_rank
+    st = stacks["ref"]
     ref = {}
     ref[srg.FAMILY_QKV] = oracle.reference_family(acts["x_qkv"], acts["y_qkv"], offs, slots,
-                                                  stacks["A_qkv"], stacks["B_qkv"],
+                                                  st["A_qkv"], st["B_qkv"],
                                                   [w.nq, w.nkv, w.nkv], R, w.dtype, requests, token_rows)
-    ref[srg.FAMILY_O] = oracle.reference_family(acts["x_o"], acts["y_o"], offs, slots, stacks["A_o"],
-                                                stacks["B_o"], [w.hidden], R, w.dtype, requests, token_rows)
+    ref[srg.FAMILY_O] = oracle.reference_family(acts["x_o"], acts["y_o"], offs, slots, st["A_o"],
+                                                st["B_o"], [w.hidden], R, w.dtype, requests, token_rows)
     return ref
 
 

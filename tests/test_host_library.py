@@ -59,13 +59,45 @@ def test_family_shapes(name):
     assert srg.lora_family_shape(d, srg.FAMILY_O) == (w.nq, 1, (w.hidden,), w.hidden)
 
 
+def logical_from_tiled(a, rows, K):
+    """The device's A layout, read back by its index formula: element (r, k)
+    sits at ((r // 16) * (K / 8) + k // 8) * 128 + (r % 16) * 8 + k % 8 and
+    the rows added up to a multiple of 16 are zero."""
+    flat = a.reshape(-1)
+    nb = (rows + 15) // 16
+    assert flat.size == nb * 16 * K
+    r = np.arange(rows)[:, None]
+    k = np.arange(K)[None, :]
+    idx = ((r // 16) * (K // 8) + k // 8) * 128 + (r % 16) * 8 + k % 8
+    rest = np.ones(flat.size, bool)
+    rest[idx.reshape(-1)] = False
+    assert not np.any(flat[rest]), "padding rows of the tiled A layout must be zero"
+    return flat[idx]
+
+
 def _pack_both(w, rank, weights, targets="qkvo", alpha=None, rs=None, bias_none=True, mask=None):
+    """Library pack (A converted from the device layout to [rows, K]) and
+    oracle pack of the same adapter."""
     alpha = w.lora_alpha if alpha is None else alpha
     rs = w.use_rslora if rs is None else rs
     got = srg.lora_pack_adapter(dims_of(w), rank, alpha, rs, bias_none, targets, weights, mask)
     want = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank,
                                w.dtype, rank, alpha, rs, bias_none, targets, weights, mask)
+    R = w.max_lora_rank
+    got = dict(got)
+    got["A_qkv"] = logical_from_tiled(got["A_qkv"], 3 * R, w.hidden)
+    got["A_o"] = logical_from_tiled(got["A_o"], R, w.nq)
     return got, want
+
+
+def test_tile_helpers_follow_the_layout_formula():
+    rng = np.random.default_rng(3)
+    for rows, K in ((48, 64), (24, 40), (16, 8), (8, 16), (96, 136)):
+        a = rng.standard_normal((rows, K)).astype(np.float32)
+        t = srg.tile_a(a)
+        assert t.shape == srg.a_tiled_shape(rows, K)
+        assert np.array_equal(logical_from_tiled(t, rows, K), a)
+        assert np.array_equal(srg.untile_a(t, rows), a)
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
