@@ -123,6 +123,7 @@ template <> struct Vec8<uint16_t> {
         b.st16(off, v);
     }
     static __device__ __forceinline__ Raw load_raw(const uint16_t* p) { return ld16(p); }
+    static __device__ __forceinline__ void store_raw(uint16_t* p, const Raw& v) { st16(p, v); }
     static __device__ __forceinline__ void unpack(const Raw& v, float* f)
     {
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -170,6 +171,11 @@ template <> struct Vec8<float> {
                                     __float_as_uint(f[7])));
     }
     static __device__ __forceinline__ Raw load_raw(const float* p) { return Raw{ld16(p), ld16(p + 4)}; }
+    static __device__ __forceinline__ void store_raw(float* p, const Raw& v)
+    {
+        st16(p, v.a);
+        st16(p + 4, v.b);
+    }
     static __device__ __forceinline__ void unpack(const Raw& v, float* f)
     {
         f[0] = __uint_as_float(v.a.x); f[1] = __uint_as_float(v.a.y);
@@ -297,53 +303,82 @@ struct ShrinkArgs {
 // [c0, c1) are nbk <= 4 blocks of 16 A rows; the four waves take one block
 // each (nbk >= 3) or split the K range 4 / nbk ways per block.  Lane
 // (g = lane / 16, r = lane % 16) owns column 16 b + r and the K pieces
-// g, g + 4, g + 8, ... of its wave's range, so the four 16-lane groups read
-// four consecutive pieces of the tiled A: one contiguous run per load.  The
-// x piece of a token is the same for the 16 lanes of a group.  Tokens go
-// eight at a time; two xor steps over lane bits 4 and 5 add the four K
-// groups, and the K-split waves are added in wave order through LDS
-// (res: [4][kTileM][16 nbk] fp32).  Rows past the tile read as zero.
+// (8 elements) g, g + 4, g + 8, ... of its wave's range, so the four 16-lane
+// groups read four consecutive pieces of the tiled A: one contiguous run per
+// load.  The range goes in chunks of kValuChunk pieces: each lane first
+// issues the loads of its A pieces of the chunk, then the workgroup stages
+// the chunk's x pieces of eight tokens in LDS with coalesced loads, and the
+// lanes read x from there (the 16 lanes of a group read the same piece).
+// Two xor steps over lane bits 4 and 5 add the four K groups; the K-split
+// waves are added in wave order through LDS (res: [4][kTileM][16 nbk]).
+// Rows past the tile read as zero.
+constexpr int kValuChunk = 32;            // pieces per chunk
+constexpr int kValuPer = kValuChunk / 4;  // pieces per lane and chunk
+
 template <typename T>
 __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int k1, int c0,
-                            int c1, float* dst, int64_t dst_ld, float* res)
+                            int c1, float* dst, int64_t dst_ld, float* res, T* xs)
 {
     constexpr int E = sizeof(T);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, r = lane & 15;
     const int cw = c1 - c0, nbk = (cw + 15) >> 4;
     const int kparts = 4 / nbk;
     const int b = w % nbk, kp = w / nbk;
     const int ldr = 16 * nbk;
-    // pieces (8 elements) of the workgroup's K range, split over kparts waves
+    const bool active = kp < kparts;  // with three blocks the fourth wave idles
+    // pieces of the workgroup's K range; wave kp takes the chunks' slices
+    // [kp * per, (kp + 1) * per) of every chunk
     const int pw0 = k0 >> 3, pw1 = (k1 + 7) >> 3;
-    const int per = (pw1 - pw0 + kparts - 1) / kparts;
-    const int q0 = pw0 + kp * per, q1 = min(q0 + per, pw1);
+    const int per = kValuChunk / kparts;  // pieces of a chunk per wave
     const T* X = reinterpret_cast<const T*>(a.x) + (size_t)ti.t0 * a.ldx;
-    const T* Ab = reinterpret_cast<const T*>(a.A) + (size_t)ti.slot * a.a_slot + (size_t)((c0 >> 4) + b) * 16 * a.in_f;
+    const T* Ab = reinterpret_cast<const T*>(a.A) + (size_t)ti.slot * a.a_slot +
+                  (size_t)((c0 >> 4) + b) * 16 * a.in_f;
     const Buf xb(X, (uint32_t)(ti.n * a.ldx * E));
     const Buf ab(Ab, (uint32_t)(16 * a.in_f * E));
-    const bool active = kp < kparts;  // with three blocks the fourth wave idles
     for (int tb = 0; tb < ti.n; tb += 8) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             acc[i] = 0.f;
-        if (active) {
-#pragma unroll 2
-            for (int p = q0 + g; p < q1; p += 4) {
-                float av[8];
-                Vec8<T>::unpack(Vec8<T>::load_raw(ab, (uint32_t)((p * 16 + r) * 8) * E), av);
-                typename Vec8<T>::Raw xr[8];
+        for (int cb = pw0; cb < pw1; cb += kValuChunk) {
+            // A pieces of this lane: cb + kp * per + g + 4 j, j < per / 4
+            typename Vec8<T>::Raw aq[kValuPer];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    xr[i] = Vec8<T>::load_raw(xb, (uint32_t)((tb + i) * a.ldx + 8 * p) * E);
+            for (int j = 0; j < kValuPer; ++j) {
+                const int pl = kp * per + g + 4 * j, p = cb + pl;
+                aq[j] = Vec8<T>::load_raw(
+                    ab, (active && 4 * j < per && p < pw1) ? (uint32_t)((p * 16 + r) * 8) * E : kOOB);
+            }
+            // x pieces of eight tokens: xs[token][piece] (rows past the tile are zero)
+            typename Vec8<T>::Raw xr[8 * kValuChunk / kThreads];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float xv[8];
-                    Vec8<T>::unpack(xr[i], xv);
+            for (int j = 0; j < 8 * kValuChunk / kThreads; ++j) {
+                const int e = tid + kThreads * j, i = e / kValuChunk, pc = e - i * kValuChunk;
+                xr[j] = Vec8<T>::load_raw(
+                    xb, cb + pc < pw1 ? (uint32_t)((tb + i) * a.ldx + 8 * (cb + pc)) * E : kOOB);
+            }
+            __syncthreads();  // the previous chunk's readers are done with xs
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[i] = fmaf(av[e], xv[e], acc[i]);
+            for (int j = 0; j < 8 * kValuChunk / kThreads; ++j) {
+                const int e = tid + kThreads * j;
+                Vec8<T>::store_raw(xs + 8 * e, xr[j]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kValuPer; ++j) {
+                const int pl = kp * per + g + 4 * j;
+                if (active && 4 * j < per && cb + pl < pw1) {
+                    float av[8];
+                    Vec8<T>::unpack(aq[j], av);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        float xv[8];
+                        Vec8<T>::unpack(Vec8<T>::load_raw(xs + 8 * (i * kValuChunk + pl)), xv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[i] = fmaf(av[e], xv[e], acc[i]);
+                    }
                 }
             }
         }
@@ -362,7 +397,7 @@ __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < ti.n * cw; e += kThreads) {
+    for (int e = tid; e < ti.n * cw; e += kThreads) {
         const int t = e / cw, c = e - t * cw;
         float v = res[t * ldr + c];
         for (int k = 1; k < kparts; ++k)
@@ -507,7 +542,8 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
     constexpr int KC = kShrinkKC;
     constexpr bool kHasValu = MODE != kValuOnly ? MODE == kMixed : true;
     constexpr bool kHasMfma = MODE != kValuOnly;
-    constexpr int kValuLds = 4 * kTileM * 16 * 4;  // shrink_valu's res
+    constexpr int kValuRes = 4 * kTileM * 16 * 4;  // shrink_valu's res
+    constexpr int kValuLds = kValuRes + 8 * kValuChunk * 8 * (int)sizeof(T);  // + its x chunk
     constexpr int kLdsBytes = (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0) > (kHasValu ? kValuLds : 0)
                                   ? (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0)
                                   : (kHasValu ? kValuLds : 0);
@@ -536,7 +572,8 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
         }
     }
     if constexpr (kHasValu)
-        shrink_valu<T>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<float*>(smem));
+        shrink_valu<T>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<float*>(smem),
+                       reinterpret_cast<T*>(smem + kValuRes));
 }
 
 // u = sum of the S slabs, in split order; 4 floats per thread.
