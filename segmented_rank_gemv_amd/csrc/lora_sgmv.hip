@@ -1065,12 +1065,29 @@ struct FusedArgs {
 };
 
 // STEPS = K steps a wave keeps in flight per batch (register budget).
-template <int NH, int STEPS>
+// XLDS: x goes through LDS (the wave's whole K range in one batch of 8
+// steps, i.e. wave_steps <= 8).  Each wave moves its 16 rows x 512 bytes of
+// x with eight LDS-DMA loads of whole 128-byte lines (2 rows per load); in
+// each line the 16-byte pieces are rotated by (row mod 8), so that the MFMA
+// operand reads (16 rows of one piece column) fall on distinct LDS banks.
+// Lanes whose piece lies past the tile's rows or the wave's K range load a
+// valid in-range piece instead: its row's results are never stored, and past
+// the K range A reads as zero.
+constexpr int kXLdsSteps = 8;
+constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x 32 bf16
+
+template <int NH, int STEPS, bool XLDS>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
     constexpr int R = 16 * NH;
-    __shared__ float part[kFusedWaves * kFusedTileM * R];  // per-wave partial u
-    __shared__ float us[kFusedTileM * R];                  // u of the tile
+    constexpr int kPartBytes = kFusedWaves * kFusedTileM * R * 4;
+    constexpr int kXBytes = XLDS ? kFusedWaves * kXLdsWaveBytes : 0;
+    static_assert(!XLDS || STEPS == kXLdsSteps, "x staging covers one batch of 8 steps");
+    // x staging (XLDS) and, after the K loop, the per-wave partial u share
+    // the first region
+    __shared__ __attribute__((aligned(16))) char smem[(kXBytes > kPartBytes ? kXBytes : kPartBytes)];
+    __shared__ float us[kFusedTileM * R];  // u of the tile
+    float* part = reinterpret_cast<float*>(smem);
 
     const int b = blockIdx.x;
     const int k = b / kXcds;
@@ -1118,29 +1135,73 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb)
         acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
-    for (int bt = 0; bt < nbatch; ++bt) {
-        uint4 xr[STEPS], ar[STEPS][NH];
+    if constexpr (XLDS) {
+        // x: eight LDS-DMA loads of 2 rows x 512 bytes into the wave's region
+        char* xw = smem + w * kXLdsWaveBytes;
+        {
+            const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
+            const Buf xv(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));
 #pragma unroll
-        for (int i = 0; i < STEPS; ++i) {
-            const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
-            const bool ok = kk < kw1;
-            xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
-            // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
+            for (int i = 0; i < kXLdsSteps; ++i) {
+                const int row = 2 * i + h;
+                const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
+                const int kk = kw0 + 8 * c;
+                const int rr = min(row, ti.n - 1);
+                const int kc = kk < kw1 ? kk : kw0;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
+                    (int)((rr * a.ldx + kc) * 2), 0, 0, 0);
+            }
+        }
+        uint4 ar[kXLdsSteps][NH];
+#pragma unroll
+        for (int i = 0; i < kXLdsSteps; ++i) {
+            const int kk = kw0 + 32 * i + 8 * q;
             const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
 #pragma unroll
             for (int nb = 0; nb < NH; ++nb)
-                ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+                ar[i][nb] = ab.ld16(kk < kw1 ? nb * ablk + ao : kOOB);
         }
-        // keep every load of the batch ahead of the first MFMA: one round trip
+        // every load (y, B, x, A) is out before the first wait: one round trip
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < STEPS; ++i)
+        for (int i = 0; i < kXLdsSteps; ++i) {
+            // piece 4 i + q of row l16: load l16 / 2, half l16 % 2, rotated slot
+            const int c = 4 * i + q;
+            const int slot = 32 * (l16 & 1) + 8 * (c >> 3) + ((c + l16) & 7);
+            const uint4 xr = *reinterpret_cast<const uint4*>(xw + 1024 * (l16 >> 1) + 16 * slot);
 #pragma unroll
             for (int nb = 0; nb < NH; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr),
                                                                   __builtin_bit_cast(bf16x8_t, ar[i][nb]),
                                                                   acc[nb], 0, 0, 0);
+        }
+        __syncthreads();  // every wave is done with its x region before part overwrites it
+    } else {
+        const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
+        for (int bt = 0; bt < nbatch; ++bt) {
+            uint4 xr[STEPS], ar[STEPS][NH];
+#pragma unroll
+            for (int i = 0; i < STEPS; ++i) {
+                const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
+                const bool ok = kk < kw1;
+                xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
+                // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
+                const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
+#pragma unroll
+                for (int nb = 0; nb < NH; ++nb)
+                    ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+            }
+            // keep every load of the batch ahead of the first MFMA: one round trip
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < STEPS; ++i)
+#pragma unroll
+                for (int nb = 0; nb < NH; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
+                                                                      __builtin_bit_cast(bf16x8_t, ar[i][nb]),
+                                                                      acc[nb], 0, 0, 0);
+        }
     }
     // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
 #pragma unroll
@@ -1475,10 +1536,20 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         return LORA_OK;
     if (grid > 2147483647LL)
         return LORA_ERR_INVALID_ARGUMENT;
-    if (c.fs.R == 16)
-        hipLaunchKernelGGL((fused_delta_kernel<1, 8>), dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((fused_delta_kernel<2, 4>), dim3((unsigned)grid), dim3(kFusedThreads), 0, s, a);
+    // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
+    const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
+    const dim3 g((unsigned)grid), blk(kFusedThreads);
+    if (c.fs.R == 16) {
+        if (xlds)
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true>), g, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false>), g, blk, 0, s, a);
+    } else {
+        if (xlds)
+            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true>), g, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false>), g, blk, 0, s, a);
+    }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 

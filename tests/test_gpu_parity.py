@@ -172,6 +172,29 @@ def test_one_kernel_delta_odd_widths_and_long_k(R, path):
     assert ey <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("R", [16, 32])
+@pytest.mark.parametrize("hidden,heads,kv,hd", [(4096, 32, 8, 128), (2080, 16, 16, 130)])
+def test_one_kernel_delta_x_through_lds(R, hidden, heads, kv, hd):
+    """One-kernel delta with x staged through LDS (K <= 4096): K = 4096 gives
+    every wave a full 256-element range; K = 2080 gives 160-element ranges
+    (lanes past the range load a clamped piece that must not contribute) and
+    32-feature tiles.  Groups of 1..32 tokens: tiles of 1..16 rows (rows past
+    the tile load a clamped row that must not be stored)."""
+    base = synth.get_workload("decode")
+    w = synth.Workload(**{**base.__dict__, "hidden": hidden, "n_heads": heads, "n_kv_heads": kv,
+                          "head_dim": hd, "max_lora_rank": R, "max_num_loras": 5})
+    lengths = np.array([1, 7, 16, 17, 32, 3, 0, 2], np.int64)
+    slots = np.array([0, 1, 2, 3, 4, -1, 2, 0], np.int32)
+    stacks = pack_stacks(w, 0, np.array([R, 8, R // 2, R, 8], np.int32))
+    acts = synth.draw_activations(w, 0, int(lengths.sum()))
+    log(f"[x-lds] R={R} hidden={hidden}")
+    gl = GpuLayer(w, stacks, lengths, slots, acts)
+    gl.run(srg.PATH_FUSED, fused=True)
+    ey, _ = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts), check_u=False)
+    log(f"[x-lds] R={R} hidden={hidden} y_rel={ey:.3e}")
+    assert ey <= TOL["bf16"]
+
+
 def test_one_kernel_path_rejected_where_it_does_not_apply():
     """PATH_FUSED: an error (no launch) for fp32, for rank 64 and for the
     split calls; y stays as it was."""
