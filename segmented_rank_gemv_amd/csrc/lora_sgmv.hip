@@ -695,29 +695,47 @@ __device__ __forceinline__ void stage_u(const ExpandArgs& a, const TileInfo& ti,
 // group q) holds features 32p + 8q .. 32p + 8q + 7 across the two
 // accumulators, and y is the C operand.
 //
-// y moves through LDS: the workgroup loads its [64 x ft] tile of y with
-// coalesced 16-byte runs (every row segment a whole number of 128-byte
-// lines), the waves read their MFMA C operands from LDS and write the
-// results back in place, and the tile is stored with the same coalesced
+// y and B move through LDS: the workgroup loads its [64 x ft] tile of y and
+// its [ft x R] tile of B with coalesced 16-byte runs (whole 128-byte lines),
+// the waves read their MFMA operands from LDS and write the results back
+// into the y tile in place, and the tile is stored with the same coalesced
 // runs.  Reading y in the MFMA layout directly would split every line over
-// two instructions (16 rows x 64 bytes each) and double the line requests.
-// y and (for NH == 1) B fragments are loaded before u is staged.
+// two instructions (16 rows x 64 bytes each), and every wave would fetch all
+// of B.  The 16-byte chunks of each B row are XOR-swizzled by bits of the
+// row (b_swizzle) so that a fragment read, 16 rows of one chunk column,
+// touches each LDS bank slot at most twice.  y, B and u loads all go out
+// before the first wait.
 constexpr int kYLd = kExpandCols + 8;  // padded LDS row of the y tile (bf16 elements)
+
+template <int NH>
+__device__ __forceinline__ int b_swizzle(int f)
+{
+    if constexpr (NH == 1)
+        return (f >> 3) & 1;
+    else if constexpr (NH == 2)
+        return ((f >> 1) & 1) | (((f >> 3) & 1) << 1);
+    else
+        return (f & 1) | (((f >> 1) & 1) << 1) | (((f >> 3) & 1) << 2);
+}
 
 template <int NH>
 __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
                                             const Buf& yb, int ucol0, float* us, float4* part,
-                                            uint16_t* ylds)
+                                            uint16_t* ylds, uint16_t* blds)
 {
+    static_assert(NH == 1 || NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
+    constexpr int R = 16 * NH;
+    constexpr int NCH = R / 8;                      // 16-byte chunks per B row
     constexpr int kMaxPairs = kExpandCols / 32;
-    constexpr bool kPrefetchB = NH == 1;
+    constexpr int BR = kExpandCols * NCH / kThreads;  // B chunks per thread for the largest tile
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, q = lane >> 4;
     const int np = a.ft >> 5;
-    const int pieces = a.ft >> 3;  // 16-byte pieces per row of the tile
+    const int pieces = a.ft >> 3;  // 16-byte pieces per row of the y tile
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0
-    const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * a.R;
+    const Buf bb(reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * R,
+                 (uint32_t)(a.ft * R * 2));
 
     // coalesced y tile: 64 rows x `pieces` pieces, kMaxPairs rounds of 256 pieces
     uint4 yraw[kMaxPairs];
@@ -726,18 +744,14 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
         const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
         yraw[i] = yb.ld16(i < np ? (uint32_t)(row * a.ldy + f0 + 8 * pc) * 2 : kOOB);
     }
-    uint4 bfr[kPrefetchB ? kMaxPairs : 1][2][NH];
-    if constexpr (kPrefetchB) {
+    // coalesced B tile: ft rows x NCH chunks (past the tile: kOOB)
+    uint4 braw[BR];
 #pragma unroll
-        for (int p = 0; p < kMaxPairs; ++p)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int kh = 0; kh < NH; ++kh)
-                    bfr[p][h][kh] = ld16(Bb + (size_t)(min(p, np - 1) * 32 + mrow + 4 * h) * a.R + 16 * kh +
-                                         8 * (q & 1));
+    for (int i = 0; i < BR; ++i) {
+        const int p = tid + kThreads * i;
+        braw[i] = bb.ld16(p < a.ft * NCH ? (uint32_t)p * 16 : kOOB);
     }
-    // u first: its loads go out before the wait on y
+    // u next: its loads go out before the wait on y and B
     stage_u(a, ti, ucol0, us, part);
 #pragma unroll
     for (int i = 0; i < kMaxPairs; ++i) {
@@ -745,6 +759,12 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
             const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
             *reinterpret_cast<uint4*>(ylds + row * kYLd + 8 * pc) = yraw[i];
         }
+    }
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+        const int p = tid + kThreads * i, f = p / NCH, c = p % NCH;
+        if (p < a.ft * NCH)
+            *reinterpret_cast<uint4*>(blds + f * R + 8 * (c ^ b_swizzle<NH>(f))) = braw[i];
     }
     __syncthreads();
 
@@ -754,7 +774,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
         bf16x8_t uf[NH];
 #pragma unroll
         for (int kh = 0; kh < NH; ++kh) {
-            const float* up = us + min(t, ti.n - 1) * a.R + 16 * kh + 8 * (q & 1);
+            const float* up = us + min(t, ti.n - 1) * R + 16 * kh + 8 * (q & 1);
             uint32_t pk[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -776,15 +796,12 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
                 f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
 #pragma unroll
                 for (int kh = 0; kh < NH; ++kh) {
-                    uint4 b0, b1;
-                    if constexpr (kPrefetchB) {
-                        b0 = bfr[p][0][kh];
-                        b1 = bfr[p][1][kh];
-                    } else {
-                        const uint16_t* bp = Bb + (size_t)(p * 32 + mrow) * a.R + 16 * kh + 8 * (q & 1);
-                        b0 = ld16(bp);
-                        b1 = ld16(bp + 4 * a.R);
-                    }
+                    const int c = 2 * kh + (q & 1);
+                    const int f0r = 32 * p + mrow, f1r = f0r + 4;
+                    const uint4 b0 =
+                        *reinterpret_cast<const uint4*>(blds + f0r * R + 8 * (c ^ b_swizzle<NH>(f0r)));
+                    const uint4 b1 =
+                        *reinterpret_cast<const uint4*>(blds + f1r * R + 8 * (c ^ b_swizzle<NH>(f1r)));
                     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[kh], acc0,
                                                                   0, 0, 0);
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[kh], acc1,
@@ -811,8 +828,9 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
     }
 }
 
-// MFMA path with y in registers (ranks 32 and 64, whose B fragments do not
-// fit a register prefetch).  Wave w owns tokens 16w .. 16w+15 of the tile and walks
+// MFMA path with y in registers (ranks 32 to 64, for which LDS tiles of y
+// and B would leave one or two workgroups per CU).  Wave w owns tokens
+// 16w .. 16w+15 of the tile and walks
 // the feature tile in pairs of 16-feature MFMA blocks.  For each 16 ranks one
 // v_mfma_f32_16x16x32_bf16 per block computes B·u with K = 32 = 16 ranks of
 // the high bf16 half of u followed by the same 16 ranks of its low half
@@ -996,6 +1014,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     float* us = smem;                                             // [kTileM][R]
     float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads]
     uint16_t* ylds = reinterpret_cast<uint16_t*>(part + kThreads);  // [kTileM][kYLd] (MFMA path)
+    uint16_t* blds = ylds + kTileM * kYLd;                            // [kExpandCols][R] (MFMA path)
 
     const int lin = blockIdx.x;
     const int ftile = lin % a.n_ftiles;
@@ -1006,15 +1025,17 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     const int f0 = ftile * a.ft;
     const int ucol0 = slice_of(a, f0) * a.R;
     const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
+    // rank 16 stages y and B in LDS; larger ranks keep y in registers (the
+    // LDS tiles would cut the workgroups per CU to two or one)
     if constexpr (NH > 0 && MODE == kMfmaOnly) {
         if constexpr (NH == 1)
-            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
+            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
         else
             expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
     } else if constexpr (NH > 0 && MODE == kMixed) {
         if (ti.glen > a.valu_max) {
             if constexpr (NH == 1)
-                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
+                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
             else
                 expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
         } else
@@ -1443,7 +1464,7 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
         return LORA_ERR_INVALID_ARGUMENT;
     const int nh = nh_possible(c, a) ? c.fs.R / 16 : 0;
     const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4) +
-                       (nh == 1 ? (size_t)kTileM * kYLd * sizeof(uint16_t) : 0);
+                       (nh == 1 ? ((size_t)kTileM * kYLd + (size_t)kExpandCols * c.fs.R) * sizeof(uint16_t) : 0);
     const dim3 g((unsigned)grid), b(kThreads);
     const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
 #define LORA_EXPAND_NH(NHV)                                                                       \
