@@ -1,0 +1,55 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU guard and the
+counter-traffic summary (calibration against a plain copy of known size)."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_counters(path, counter, copy_kib, kern_rows):
+    names = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+             "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+             "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+             "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=names)
+        wr.writeheader()
+        rows = [("__amd_rocclr_copyBuffer", copy_kib)] * 3 + [("__amd_rocclr_copyBuffer", 0.5)]
+        rows += kern_rows
+        for i, (name, v) in enumerate(rows):
+            wr.writerow({**{k: 0 for k in names}, "Dispatch_Id": i, "Kernel_Name": name,
+                         "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    import bench
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    k1 = "void lora::(anonymous namespace)::shrink_kernel<unsigned short, 3, 1>(lora::ShrinkArgs)"
+    k2 = "lora::(anonymous namespace)::reduce_slabs(float const*, long, int, float*, long)"
+    f = tmp_path / "fetch.csv"
+    w = tmp_path / "write.csv"
+    # copy of 256 MiB: FETCH reads half (128 MiB), WRITE reads all
+    _write_counters(f, "FETCH_SIZE", 131072.0, [(k1, 1000.0), (k1, 1000.0), (k2, 10.0), (k2, 10.0)])
+    _write_counters(w, "WRITE_SIZE", 262144.0, [(k1, 20.0), (k1, 20.0), (k2, 5.0), (k2, 5.0)])
+    args = type("A", (), {"traffic_from": [str(f), str(w)], "traffic_kind": "shrink_qkv",
+                          "workload": "prefill"})()
+    bench.summarize_traffic(args)
+    out = json.load(open(tmp_path / "traffic.json"))
+    assert out["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert out["copy_calibration"]["write_factor"] == pytest.approx(1.0)
+    # per call: (1000 + 10) KiB fetched x 2 + (20 + 5) KiB written
+    want = (1010.0 * 2 + 25.0) * 1024
+    assert out["kernels"]["prefill:shrink_qkv"]["hbm_bytes_per_launch"] == pytest.approx(want)

@@ -195,6 +195,29 @@ def test_one_kernel_delta_x_through_lds(R, hidden, heads, kv, hd):
     assert ey <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("path", ["auto", "valu", "mfma"])
+def test_largest_rank(path):
+    """max_lora_rank 128 (the largest the kernels accept): the QKV shrink
+    spans six 64-column groups, the expand runs on the VALU path (MFMA
+    expand stops at rank 64) and the one-kernel path does not apply."""
+    w = small_bf16(L=3, R=128)
+    lengths = np.array([5, 70, 1, 33], np.int64)
+    slots = np.array([2, 0, -1, 1], np.int32)
+    if path == "mfma":
+        # the forced MFMA path needs an MFMA expand: rank 128 is rejected up front
+        stacks = pack_stacks(w, 0, np.array([128, 100, 7], np.int32))
+        acts = synth.draw_activations(w, 0, int(lengths.sum()))
+        gl = GpuLayer(w, stacks, lengths, slots, acts)
+        with pytest.raises(srg.LoraError):
+            srg.lora_sgmv_expand(gl.dims, srg.FAMILY_QKV, gl.u[srg.FAMILY_QKV], gl.st["B_qkv"],
+                                 gl.routing["host"], gl.dev["y_qkv"], srg.PATH_MFMA)
+        return
+    gl, ref, _ = run_custom(w, lengths, slots, PATHS[path], ranks=np.array([128, 100, 7], np.int32))
+    ey, eu = compare(w, gl, ref)
+    log(f"[rank128] path={path} y_rel={ey:.3e} u_rel={eu:.3e}")
+    assert ey <= TOL["bf16"] and eu <= U_TOL["bf16"]
+
+
 def test_one_kernel_path_rejected_where_it_does_not_apply():
     """PATH_FUSED: an error (no launch) for fp32, for rank 64 and for the
     split calls; y stays as it was."""
