@@ -828,6 +828,100 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
     }
 }
 
+// MFMA path for ranks 32 and 64: B through LDS, y in registers.  The
+// workgroup loads its [ft x R] tile of B with coalesced 16-byte runs into
+// LDS (chunks XOR-swizzled per row, as in expand_mfma) and the waves read
+// their M-operand fragments from there; y stays in registers in the MFMA
+// layout as in expand_mfma_reg.  Reading B fragments straight from memory
+// touches 16 rows per instruction and leans on L1 reuse across the rank
+// steps and the four waves, which breaks down once several workgroups share
+// a CU; an LDS tile of y as well would cut the workgroups per CU to one or
+// two.  Waves with no token in the tile help with the B tile only.
+template <int NH>
+__device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileInfo& ti, int f0,
+                                               const Buf& yb, int ucol0, float* us, float4* part,
+                                               uint16_t* blds)
+{
+    static_assert(NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
+    constexpr int R = 16 * NH;
+    constexpr int NCH = R / 8;                        // 16-byte chunks per B row
+    constexpr int kMaxPairs = kExpandCols / 32;
+    constexpr int BR = kExpandCols * NCH / kThreads;  // B chunks per thread for the largest tile
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int np = a.ft >> 5;
+    const int t = 16 * w + l16;
+    const bool tok = t < ti.n;
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0
+    const Buf bb(reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * R,
+                 (uint32_t)(a.ft * R * 2));
+
+    uint4 yraw[kMaxPairs];
+#pragma unroll
+    for (int p = 0; p < kMaxPairs; ++p)
+        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
+    uint4 braw[BR];
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+        const int p = tid + kThreads * i;
+        braw[i] = bb.ld16(p < a.ft * NCH ? (uint32_t)p * 16 : kOOB);
+    }
+    stage_u(a, ti, ucol0, us, part);
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+        const int p = tid + kThreads * i, f = p / NCH, c = p % NCH;
+        if (p < a.ft * NCH)
+            *reinterpret_cast<uint4*>(blds + f * R + 8 * (c ^ b_swizzle<NH>(f))) = braw[i];
+    }
+    __syncthreads();
+    if (16 * w >= ti.n)
+        return;
+
+    // u fragments: lanes q<2 carry hi(u[t][16kh+8q..]), lanes q>=2 lo(u[t][16kh+8(q-2)..])
+    bf16x8_t uf[NH];
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) {
+        const float* up = us + min(t, ti.n - 1) * R + 16 * kh + 8 * (q & 1);
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = up[2 * e], v1 = up[2 * e + 1];
+            uint32_t hi = f2bf_pair(v0, v1);
+            if (q >= 2)
+                hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+            pk[e] = hi;
+        }
+        uf[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+
+#pragma unroll
+    for (int p = 0; p < kMaxPairs; ++p) {
+        if (p < np) {
+            const uint4 yv = yraw[p];
+            f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
+            f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+#pragma unroll
+            for (int kh = 0; kh < NH; ++kh) {
+                const int c = 2 * kh + (q & 1);
+                const int f0r = 32 * p + mrow, f1r = f0r + 4;
+                const uint4 b0 = *reinterpret_cast<const uint4*>(blds + f0r * R + 8 * (c ^ b_swizzle<NH>(f0r)));
+                const uint4 b1 = *reinterpret_cast<const uint4*>(blds + f1r * R + 8 * (c ^ b_swizzle<NH>(f1r)));
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[kh], acc0,
+                                                              0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[kh], acc1,
+                                                              0, 0, 0);
+            }
+            uint4 o;
+            o.x = f2bf_pair(acc0[0], acc0[1]);
+            o.y = f2bf_pair(acc0[2], acc0[3]);
+            o.z = f2bf_pair(acc1[0], acc1[1]);
+            o.w = f2bf_pair(acc1[2], acc1[3]);
+            yb.st16(tok ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
+        }
+    }
+}
+
 // MFMA path with y in registers (ranks 32 to 64, for which LDS tiles of y
 // and B would leave one or two workgroups per CU).  Wave w owns tokens
 // 16w .. 16w+15 of the tile and walks
@@ -1013,8 +1107,10 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     extern __shared__ float smem[];
     float* us = smem;                                             // [kTileM][R]
     float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads]
-    uint16_t* ylds = reinterpret_cast<uint16_t*>(part + kThreads);  // [kTileM][kYLd] (MFMA path)
-    uint16_t* blds = ylds + kTileM * kYLd;                            // [kExpandCols][R] (MFMA path)
+    // MFMA path, rank 16: y tile [kTileM][kYLd], then B tile [kExpandCols][R];
+    // ranks 32 and 64: B tile alone, at ylds
+    uint16_t* ylds = reinterpret_cast<uint16_t*>(part + kThreads);
+    uint16_t* blds = ylds + kTileM * kYLd;
 
     const int lin = blockIdx.x;
     const int ftile = lin % a.n_ftiles;
@@ -1025,17 +1121,22 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     const int f0 = ftile * a.ft;
     const int ucol0 = slice_of(a, f0) * a.R;
     const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
-    // rank 16 stages y and B in LDS; larger ranks keep y in registers (the
-    // LDS tiles would cut the workgroups per CU to two or one)
+    // rank 16 stages y and B in LDS; ranks 32 and 64 stage B alone and keep y
+    // in registers (an LDS tile of y as well would cut the workgroups per CU
+    // to two or one); rank 48 reads both from memory
     if constexpr (NH > 0 && MODE == kMfmaOnly) {
         if constexpr (NH == 1)
             expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
+        else if constexpr (NH == 2 || NH == 4)
+            expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
         else
             expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
     } else if constexpr (NH > 0 && MODE == kMixed) {
         if (ti.glen > a.valu_max) {
             if constexpr (NH == 1)
                 expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
+            else if constexpr (NH == 2 || NH == 4)
+                expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
             else
                 expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
         } else
@@ -1426,7 +1527,10 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
     a.kc = plan.kc;
     a.nz = plan.nz;
     a.cb = plan.cb;
-    a.valu_max = valu_max_for(path, shrink_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_SHRINK", 8));
+    // ranks 32 and up take the MFMA path for every tile: the VALU path keeps
+    // one chunk in flight and runs eight token rows per chunk whatever the
+    // tile's length, which loses to the MFMA tile even for one-token groups
+    a.valu_max = valu_max_for(path, shrink_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_SHRINK", c.fs.R >= 32 ? 0 : 8));
     a.r = c.r;
     const int64_t grid = (int64_t)plan.n_tiles * plan.S * plan.nz;
     if (grid > 2147483647LL)
@@ -1456,15 +1560,22 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
         a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
     a.ft = expand_tile(c.fs);
     a.n_ftiles = c.fs.out_f / a.ft;
-    a.valu_max = valu_max_for(path, expand_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_EXPAND", 8));
+    // ranks 32 and 64 take the MFMA path (B through LDS) for every tile: the
+    // VALU path reads B rows strided and is L1-bound there
+    const bool lds_b = c.fs.R == 32 || c.fs.R == 64;
+    a.valu_max = valu_max_for(path, expand_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_EXPAND", lds_b ? 0 : 8));
     a.r = c.r;
     const int64_t tiles = ((int64_t)c.r.end + kTileM - 1) / kTileM + c.r.G;
     const int64_t grid = tiles * a.n_ftiles;
     if (grid > 2147483647LL)
         return LORA_ERR_INVALID_ARGUMENT;
     const int nh = nh_possible(c, a) ? c.fs.R / 16 : 0;
+    // u tile, slab partial sums, then the LDS tiles of the MFMA path: y and B
+    // (rank 16) or B alone (ranks 32 and 64)
     const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4) +
-                       (nh == 1 ? ((size_t)kTileM * kYLd + (size_t)kExpandCols * c.fs.R) * sizeof(uint16_t) : 0);
+                       (nh == 1   ? ((size_t)kTileM * kYLd + (size_t)kExpandCols * c.fs.R) * sizeof(uint16_t)
+                        : nh == 2 || nh == 4 ? (size_t)kExpandCols * c.fs.R * sizeof(uint16_t)
+                                             : 0);
     const dim3 g((unsigned)grid), b(kThreads);
     const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
 #define LORA_EXPAND_NH(NHV)                                                                       \
