@@ -1169,6 +1169,14 @@ constexpr int kFusedTileM = 16;
 constexpr int kFusedMaxFeat = 32 * kFusedWaves;  // one 32-feature pair per wave
 constexpr int kXcds = 8;
 
+// A token tile as the host lays it out from its copy of the routing (the
+// same tiles locate_tile<kFusedTileM, true> finds).
+struct TileEntry {
+    int t0, n, slot, glen;
+};
+constexpr int kFusedHostTiles = 128;
+constexpr int kFusedHostFt = 64;
+
 struct FusedArgs {
     const uint16_t* x;
     int64_t ldx;
@@ -1184,6 +1192,8 @@ struct FusedArgs {
     int nf;          // feature tiles per token tile
     int wave_steps;  // 32-element K steps per wave
     RouteArgs r;
+    TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
+    int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT)
 };
 
 // STEPS = K steps a wave keeps in flight per batch (register budget).
@@ -1198,7 +1208,9 @@ struct FusedArgs {
 constexpr int kXLdsSteps = 8;
 constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x 32 bf16
 
-template <int NH, int STEPS, bool XLDS>
+// HOSTT: the tile comes from the host-built table tt (entries with n = 0
+// pad the grid), else from locate_tile over the routing.
+template <int NH, int STEPS, bool XLDS, bool HOSTT>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
     constexpr int R = 16 * NH;
@@ -1211,19 +1223,43 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     __shared__ float us[kFusedTileM * R];  // u of the tile
     float* part = reinterpret_cast<float*>(smem);
 
-    const int b = blockIdx.x;
-    const int k = b / kXcds;
-    const int tile = (k / a.nf) * kXcds + b % kXcds;
-    const int ftile = k % a.nf;
+    // grid (kXcds * nf, tiles / kXcds): the linear block id b = x + y * gridDim.x
+    // runs over XCDs as b % kXcds, so the nf workgroups of tile y * kXcds +
+    // x % kXcds share one XCD; tile and feature tile need no kernel argument
+    const int tile = blockIdx.y * kXcds + blockIdx.x % kXcds;
+    const int ftile = blockIdx.x / kXcds;
     TileInfo ti;
-    if (!locate_tile<kFusedTileM, true>(a.r, tile, ti))
-        return;
-    int sl = 0, rem = ftile;
-    while (sl < a.n_s - 1 && rem >= a.nft[sl]) {
-        rem -= a.nft[sl];
-        ++sl;
+    int sl = 0, f0;
+    if constexpr (HOSTT) {
+        // the entries' addresses depend on blockIdx only, and nothing branches
+        // before the data loads: the argument loads take one round trip.  A
+        // padding entry has n = 0, which masks every access of the workgroup.
+        const TileEntry te = a.tt[min(tile, kFusedHostTiles - 1)];
+        const int2 fe = a.fts[min(ftile, kFusedHostFt - 1)];
+        ti.g = 0;
+        ti.t0 = te.t0;
+        ti.n = te.n;
+        ti.slot = te.slot;
+        ti.glen = te.glen;
+        sl = fe.x;
+        f0 = fe.y;
+        // every argument the data addresses need, in scalar registers before
+        // anything else: the compiler would otherwise split the argument
+        // loads into two dependent rounds
+        asm volatile("" ::"s"(a.x), "s"(a.A), "s"(a.B), "s"(a.y), "s"(a.ldx), "s"(a.ldy), "s"(a.a_slot),
+                     "s"(a.in_f), "s"(a.out_f), "s"(a.F), "s"(a.wave_steps), "s"(te.t0), "s"(te.n), "s"(te.slot),
+                     "s"(fe.x), "s"(fe.y));
+    } else {
+        if (!locate_tile<kFusedTileM, true>(a.r, tile, ti))
+            return;
+        int rem = ftile;
+        while (sl < a.n_s - 1 && rem >= a.nft[sl]) {
+            rem -= a.nft[sl];
+            ++sl;
+        }
+        f0 = a.soff[sl] + rem * a.F;
     }
-    const int f0 = a.soff[sl] + rem * a.F;
+    const uint32_t live = ti.n > 0 ? 1u : 0u;  // 0 for a padding tile
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, q = lane >> 4;
 
@@ -1236,7 +1272,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const uint4 yraw = yb.ld16(yoff);
     // B rows as the M operand, permuted: row i of block h is feature
     // 32 w + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
-    const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, (uint32_t)(a.F * R * 2));
+    const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint4 bfr[2][NH];
 #pragma unroll
@@ -1249,7 +1285,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     // positions past the wave's range read as zero (offset kOOB).
     const Buf xb(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));  // rows >= n read zero
     // the slice's NH blocks of the tiled A: one step of one block is a 1 KB run
-    const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)sl * R * a.in_f, (uint32_t)(R * a.in_f * 2));
+    const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)sl * R * a.in_f, live * (uint32_t)(R * a.in_f * 2));
     const int kw0 = w * a.wave_steps * 32;
     const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
     const uint32_t xrow = (uint32_t)(l16 * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
@@ -1666,22 +1702,54 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds * a.nf;
     if (grid == 0)
         return LORA_OK;
-    if (grid > 2147483647LL)
+    if (grid > 2147483647LL || (tiles + kXcds - 1) / kXcds > 65535)
         return LORA_ERR_INVALID_ARGUMENT;
+    // tile table from the host routing: the tiles of locate_tile<kFusedTileM,
+    // true> (each group cut into ceil(len / 16) near-equal tiles)
+    const int64_t tiles_pad = (tiles + kXcds - 1) / kXcds * kXcds;
+    const bool hostt = c.r.kr && tiles_pad <= kFusedHostTiles && a.nf <= kFusedHostFt;
+    if (hostt) {
+        int n = 0;
+        for (int g = 0; g < c.r.G; ++g) {
+            const int gs = c.r.k_offs[g], len = c.r.k_offs[g + 1] - gs;
+            const int gnt = (len + kFusedTileM - 1) / kFusedTileM;
+            for (int j = 0; j < gnt; ++j) {
+                const int t0 = gs + (int)(((int64_t)len * j) / gnt);
+                const int t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
+                a.tt[n++] = TileEntry{t0, t1 - t0, c.r.k_ids[g], len};
+            }
+        }
+        for (; n < kFusedHostTiles; ++n)
+            a.tt[n] = TileEntry{0, 0, 0, 0};
+        int ft = 0;
+        for (int sl = 0; sl < c.fs.n_s; ++sl)
+            for (int i = 0; i < a.nft[sl]; ++i)
+                a.fts[ft++] = make_int2(sl, a.soff[sl] + i * a.F);
+        for (; ft < kFusedHostFt; ++ft)
+            a.fts[ft] = make_int2(0, 0);
+    }
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
     const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
-    const dim3 g((unsigned)grid), blk(kFusedThreads);
+    const dim3 g((unsigned)(kXcds * a.nf), (unsigned)((tiles + kXcds - 1) / kXcds)), blk(kFusedThreads);
+#define LORA_FUSED(NH, ST, XL)                                                             \
+    if (hostt)                                                                             \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, true>), g, blk, 0, s, a);       \
+    else                                                                                   \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, false>), g, blk, 0, s, a);
     if (c.fs.R == 16) {
-        if (xlds)
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true>), g, blk, 0, s, a);
-        else
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false>), g, blk, 0, s, a);
+        if (xlds) {
+            LORA_FUSED(1, 8, true)
+        } else {
+            LORA_FUSED(1, 8, false)
+        }
     } else {
-        if (xlds)
-            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true>), g, blk, 0, s, a);
-        else
-            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false>), g, blk, 0, s, a);
+        if (xlds) {
+            LORA_FUSED(2, 8, true)
+        } else {
+            LORA_FUSED(2, 4, false)
+        }
     }
+#undef LORA_FUSED
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
