@@ -1177,6 +1177,8 @@ struct TileEntry {
 constexpr int kFusedHostTiles = 128;
 constexpr int kFusedHostFt = 64;
 
+// The fields every workgroup needs before its first data load come first,
+// so that they are one contiguous run of the argument segment.
 struct FusedArgs {
     const uint16_t* x;
     int64_t ldx;
@@ -1185,12 +1187,13 @@ struct FusedArgs {
     const uint16_t* B;  // [L][out_f][R]
     uint16_t* y;
     int64_t ldy;
-    int in_f, C, out_f, n_s;
+    int in_f, out_f;
+    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat)
+    int wave_steps;  // 32-element K steps per wave
+    int C, n_s;
     int soff[5];
     int nft[4];      // feature tiles per slice
-    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat)
     int nf;          // feature tiles per token tile
-    int wave_steps;  // 32-element K steps per wave
     RouteArgs r;
     TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
     int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT)
