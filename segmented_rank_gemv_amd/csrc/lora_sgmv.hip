@@ -32,6 +32,7 @@
 // only synchronisation: no atomics, no device-scope fences, deterministic
 // results.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdlib.h>
 #include <string.h>
 
@@ -1709,21 +1710,49 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         return LORA_ERR_INVALID_ARGUMENT;
     // tile table from the host routing: the tiles of locate_tile<kFusedTileM,
     // true> (each group cut into ceil(len / 16) near-equal tiles)
-    const int64_t tiles_pad = (tiles + kXcds - 1) / kXcds * kXcds;
-    const bool hostt = c.r.kr && tiles_pad <= kFusedHostTiles && a.nf <= kFusedHostFt;
+    // The tiles of a group go to one XCD (tile position y * kXcds + xcd), so
+    // that its A and B rows are fetched into one L2: groups, largest first,
+    // each to the XCD with the fewest tiles so far.
+    int64_t rows = (tiles + kXcds - 1) / kXcds;  // grid rows (tiles per XCD)
+    bool hostt = c.r.kr && a.nf <= kFusedHostFt;
     if (hostt) {
-        int n = 0;
-        for (int g = 0; g < c.r.G; ++g) {
-            const int gs = c.r.k_offs[g], len = c.r.k_offs[g + 1] - gs;
-            const int gnt = (len + kFusedTileM - 1) / kFusedTileM;
-            for (int j = 0; j < gnt; ++j) {
-                const int t0 = gs + (int)(((int64_t)len * j) / gnt);
-                const int t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
-                a.tt[n++] = TileEntry{t0, t1 - t0, c.r.k_ids[g], len};
+        int order[LORA_MAX_HOST_GROUPS], cnt[kXcds] = {}, xcd_of[LORA_MAX_HOST_GROUPS];
+        const bool together = env_int("LORA_SGMV_XCD_GROUPS", 1) != 0;
+        for (int g = 0; g < c.r.G; ++g)
+            order[g] = g;
+        auto gtiles = [&](int g) { return (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM; };
+        if (together) {
+            std::stable_sort(order, order + c.r.G, [&](int p, int q) { return gtiles(p) > gtiles(q); });
+            for (int i = 0; i < c.r.G; ++i) {
+                int best = 0;
+                for (int x = 1; x < kXcds; ++x)
+                    if (cnt[x] < cnt[best])
+                        best = x;
+                xcd_of[order[i]] = best;
+                cnt[best] += gtiles(order[i]);
             }
+            rows = *std::max_element(cnt, cnt + kXcds);
         }
-        for (; n < kFusedHostTiles; ++n)
-            a.tt[n] = TileEntry{0, 0, 0, 0};
+        hostt = rows * kXcds <= kFusedHostTiles;
+        if (hostt) {
+            for (int i = 0; i < kFusedHostTiles; ++i)
+                a.tt[i] = TileEntry{0, 0, 0, 0};
+            int fill[kXcds] = {}, n = 0;
+            for (int g = 0; g < c.r.G; ++g) {
+                const int gs = c.r.k_offs[g], len = c.r.k_offs[g + 1] - gs;
+                const int gnt = gtiles(g);
+                for (int j = 0; j < gnt; ++j) {
+                    const int t0 = gs + (int)(((int64_t)len * j) / gnt);
+                    const int t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
+                    const int pos = together ? fill[xcd_of[g]]++ * kXcds + xcd_of[g] : n++;
+                    a.tt[pos] = TileEntry{t0, t1 - t0, c.r.k_ids[g], len};
+                }
+            }
+        } else {
+            rows = (tiles + kXcds - 1) / kXcds;
+        }
+    }
+    if (hostt) {
         int ft = 0;
         for (int sl = 0; sl < c.fs.n_s; ++sl)
             for (int i = 0; i < a.nft[sl]; ++i)
@@ -1733,7 +1762,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     }
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
     const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
-    const dim3 g((unsigned)(kXcds * a.nf), (unsigned)((tiles + kXcds - 1) / kXcds)), blk(kFusedThreads);
+    const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
 #define LORA_FUSED(NH, ST, XL)                                                             \
     if (hostt)                                                                             \
         hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, true>), g, blk, 0, s, a);       \
