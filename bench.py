@@ -379,6 +379,53 @@ def main():
     value = end * n_layers / (ms_per_step * 1e-3)
     e2e_gbs = fam_bytes * n_layers / (ms_per_step * 1e-3) / 1e9
 
+    # ---- adapter activation (outside the step): the slot cache's decisions
+    # for a stream of batches over twice as many adapters as slots, and the
+    # host-to-device writes of one adapter into one slot of every layer
+    # (lora_write_slot from pinned host memory, timed with events on the
+    # stream).  Each slot is rewritten with the adapter it already holds, so
+    # the stacks are unchanged.
+    activation = None
+    if L > 1:
+        cache = srg.LoraSlotCache(L)
+        crng = np.random.default_rng(5)
+        nb, loads = 2000, 0
+        t0 = time.perf_counter()
+        for _ in range(nb):
+            ids = crng.integers(-1, 2 * L, size=len(slots))
+            keep = [a for a in dict.fromkeys(ids.tolist()) if a >= 0][:L]
+            ids = np.where(np.isin(ids, keep), ids, -1)
+            loads += len(cache.activate_batch(ids)[1])
+        cache_us = 1e6 * (time.perf_counter() - t0) / nb
+        wl = min(n_layers, 16)
+        pinned = []
+        for l in range(wl):
+            s0 = l % L
+            pk = srg.lora_pack_adapter(dims, int(ranks[s0]), w.lora_alpha, w.use_rslora, True, "qkvo",
+                                       synth.draw_adapter(w, l, s0, int(ranks[s0])))
+            pinned.append((s0, {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16 if v.dtype == np.uint16
+                                                                                  else np.float32)).pin_memory()
+                                for k, v in pk.items()}))
+        slot_bytes = sum(v.numel() * v.element_size() for v in pinned[0][1].values())
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ea.record(stream)
+            for _ in range(reps):
+                for l, (s0, pk) in enumerate(pinned):
+                    srg.lora_write_slot(dims, s0, pk, {k: layers[l][k] for k in ("A_qkv", "B_qkv", "A_o", "B_o")},
+                                        stream=stream)
+            eb.record(stream)
+        torch.cuda.synchronize()
+        write_us = 1e3 * ea.elapsed_time(eb) / (reps * wl)
+        activation = {"slots": L, "batches": nb, "loads_per_batch": loads / nb,
+                      "cache_us_per_batch": cache_us, "slot_bytes_per_layer": slot_bytes,
+                      "write_us_per_slot_layer": write_us,
+                      "h2d_GBps": slot_bytes / (write_us * 1e-6) / 1e9}
+        log(f"activation: cache {cache_us:.2f} us/batch, write {write_us:.2f} us/slot-layer "
+            f"({activation['h2d_GBps']:.1f} GB/s)")
+
     # ---- phase 3: CPU oracle on a bounded sample: whole layers (both
     # families) of the same workload, cycling over a few distinct layers and
     # rotating which requests a layer's row budget covers, until about
@@ -453,6 +500,7 @@ def main():
                       "GBps": kbytes[k] / (avg_us[k] * 1e-6) / 1e9} for k in KINDS},
         "end_to_end_GBps": e2e_gbs,
         "pack_ms_per_adapter_layer": 1e3 * t_pack / max(n_pack, 1),
+        "activation": activation,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -56,7 +56,9 @@ enum {
     LORA_ERR_SLOT_OUT_OF_RANGE = 3, /* slot id outside [-1, max_num_loras) */
     LORA_ERR_CAPACITY = 4,          /* a caller buffer (workspace, output) is too small */
     LORA_ERR_DEVICE = 5,            /* the HIP runtime reported an error for a launch */
-    LORA_ERR_UNSPECIFIED = 6        /* anything else */
+    LORA_ERR_UNSPECIFIED = 6,       /* anything else */
+    LORA_ERR_NO_FREE_SLOT = 7,      /* every slot holds an adapter that may not be evicted ([vLLM] §5.3 "No free lora slots") */
+    LORA_ERR_NOT_ACTIVE = 8         /* the adapter holds no slot (LoRAStatus UNLOAD_NAME_NONEXISTENT) */
 };
 
 /* Element type of x, y and the adapter stacks.  Accumulation is always fp32. */
@@ -294,6 +296,89 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
                               const void* A_stack, const void* B_stack, const lora_routing_t* routing,
                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                               int32_t path, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Adapter slot cache — host, synchronous.
+ *
+ * Which adapter (a caller-chosen integer id >= 0, like vLLM's lora_int_id)
+ * occupies which of the num_slots slots of the device stacks
+ * ([vLLM] §9 lora_index_to_id; [MAX-V3] "LRU slot" of activate_adapter):
+ *   - activating an adapter that holds a slot keeps the slot and makes the
+ *     adapter the most recently used ([vLLM] §5.3 early return, §7 touch);
+ *   - a new adapter takes the lowest free slot ([vLLM] §5.3 first free slot);
+ *   - with no free slot, policy LORA_CACHE_LRU evicts the least recently used
+ *     adapter that is not pinned and reuses its slot ([MAX-V3]
+ *     activate_adapter; [vLLM] §7 remove_oldest, then activate), policy
+ *     LORA_CACHE_NO_EVICT fails with LORA_ERR_NO_FREE_SLOT ([vLLM] §5.3);
+ *   - unloading frees the slot ([MAX-V3] unload_adapter); a pinned adapter is
+ *     never evicted ([vLLM] §7 pin_adapter).
+ * A slot that needs_load must be filled (lora_write_slot) before a batch
+ * routes tokens to it.  The cache owns its host memory (lora_cache_destroy
+ * frees it); calls on one cache must not run concurrently.  On an error the
+ * cache is unchanged.
+ */
+typedef struct lora_slot_cache lora_slot_cache_t;
+enum { LORA_CACHE_LRU = 0, LORA_CACHE_NO_EVICT = 1 };
+
+/* num_slots in [1, 2^20] (normally max_num_loras).  Errors: INVALID_ARGUMENT. */
+lora_status_t lora_cache_create(int32_t num_slots, int32_t policy, lora_slot_cache_t** cache);
+void lora_cache_destroy(lora_slot_cache_t* cache);
+
+/* Activate one adapter: *slot = its slot, *needs_load = 1 when the slot must
+ * be (re)written, *evicted_id = the adapter it replaced (-1 if none).
+ * Errors: INVALID_ARGUMENT (NULL, id < 0), NO_FREE_SLOT. */
+lora_status_t lora_cache_activate(lora_slot_cache_t* cache, int64_t adapter_id, int32_t* slot,
+                                  int32_t* needs_load, int64_t* evicted_id);
+
+/* Activate the adapters of one batch ([vLLM] §4 set_active_adapters: every
+ * adapter of the batch active before the forward): adapter_ids[i] of request
+ * i (-1 = base model) becomes request_slot[i] (-1 for base), ready for
+ * lora_build_routing.  The batch's adapters that hold a slot are touched
+ * first, then the others are activated in first-appearance order; a batch
+ * never evicts its own adapters.  The slots that need loading and their
+ * adapters are listed in load_slots / load_ids (capacity num_requests),
+ * *num_loads of them.  Errors: INVALID_ARGUMENT, NO_FREE_SLOT (the batch
+ * needs more slots than the unpinned and free ones). */
+lora_status_t lora_cache_activate_batch(lora_slot_cache_t* cache, int32_t num_requests,
+                                        const int64_t* adapter_ids, int32_t* request_slot,
+                                        int32_t* load_slots, int64_t* load_ids, int32_t* num_loads);
+
+/* Free the adapter's slot (*slot = the slot it held).  Errors:
+ * INVALID_ARGUMENT, NOT_ACTIVE. */
+lora_status_t lora_cache_unload(lora_slot_cache_t* cache, int64_t adapter_id, int32_t* slot);
+
+/* pinned != 0: activate the adapter (as lora_cache_activate) and pin it;
+ * pinned == 0: unpin an active adapter (NOT_ACTIVE otherwise). */
+lora_status_t lora_cache_pin(lora_slot_cache_t* cache, int64_t adapter_id, int32_t pinned, int32_t* slot,
+                             int32_t* needs_load, int64_t* evicted_id);
+
+/* *slot = the adapter's slot, or -1 if it holds none ([MAX-V3] is_active_lora). */
+lora_status_t lora_cache_lookup(const lora_slot_cache_t* cache, int64_t adapter_id, int32_t* slot);
+
+/* slot_ids[s] = adapter in slot s or -1 ([vLLM] §9 lora_index_to_id);
+ * pinned[s] (optional) = 1 if pinned.  Errors: INVALID_ARGUMENT, CAPACITY
+ * (capacity < num_slots). */
+lora_status_t lora_cache_slot_table(const lora_slot_cache_t* cache, int32_t capacity, int64_t* slot_ids,
+                                    uint8_t* pinned);
+
+/* ---------------------------------------------------------------------------
+ * lora_write_slot / lora_reset_slot — device, asynchronous on `stream`.
+ *
+ * Write one adapter of one layer, as lora_pack_adapter laid it out in host
+ * memory, into slot `slot` of the layer's four device stacks ([vLLM] §5.3
+ * set_lora; [MAX-lora] 加载时的处理管线, last step), with host-to-device
+ * copies; or zero the slot ([vLLM] §5.3 reset_lora) with a fill kernel.
+ * Stacks: A_qkv [L][round16(3R)][hidden] and A_o [L][round16(R)][n_heads*head_dim]
+ * in the tiled layout, B_qkv [L][q+2kv][R], B_o [L][hidden][R], dims->dtype.
+ * The host buffers must stay valid until the copies have run (pinned memory
+ * makes them asynchronous).  Errors: INVALID_ARGUMENT (NULL, slot outside
+ * [0, max_num_loras)), DEVICE.
+ */
+lora_status_t lora_write_slot(const lora_dims_t* dims, int32_t slot, const void* A_qkv, const void* B_qkv,
+                              const void* A_o, const void* B_o, void* A_qkv_stack, void* B_qkv_stack,
+                              void* A_o_stack, void* B_o_stack, void* stream);
+lora_status_t lora_reset_slot(const lora_dims_t* dims, int32_t slot, void* A_qkv_stack, void* B_qkv_stack,
+                              void* A_o_stack, void* B_o_stack, void* stream);
 
 #ifdef __cplusplus
 }

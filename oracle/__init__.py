@@ -17,3 +17,4 @@ from .oracle import (  # noqa: F401
     route,
     scaling,
 )
+from .slot_cache import OracleSlotCache, SlotCacheError  # noqa: F401,E402

@@ -10,6 +10,11 @@ stream passed in).
 """
 
 from ._lib import (  # noqa: F401
+    CACHE_LRU,
+    CACHE_NO_EVICT,
+    LoraSlotCache,
+    lora_reset_slot,
+    lora_write_slot,
     DTYPE_BF16,
     DTYPE_F32,
     FAMILY_O,

@@ -21,7 +21,8 @@ _DTYPES = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
 
 class LoraError(Exception):
     """A non-zero lora_status_t.  Codes 1-4 (bad argument, invalid adapter,
-    slot out of range, capacity) also derive from ValueError."""
+    slot out of range, capacity) and 7-8 (no free slot, adapter not active)
+    also derive from ValueError."""
 
     def __init__(self, code: int, name: str, where: str):
         super().__init__(f"{where}: {name} ({code})")
@@ -148,6 +149,27 @@ def _load():
     lib.lora_sgmv_expand.argtypes = [D, i32, P, P, RT, P, i64, i32, P]
     lib.lora_sgmv_delta.restype = i32
     lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, RT, P, i64, P, ctypes.c_size_t, i32, P]
+    I32P, I64P = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.lora_cache_create.restype = i32
+    lib.lora_cache_create.argtypes = [i32, i32, ctypes.POINTER(P)]
+    lib.lora_cache_destroy.restype = None
+    lib.lora_cache_destroy.argtypes = [P]
+    lib.lora_cache_activate.restype = i32
+    lib.lora_cache_activate.argtypes = [P, i64, I32P, I32P, I64P]
+    lib.lora_cache_activate_batch.restype = i32
+    lib.lora_cache_activate_batch.argtypes = [P, i32, P, P, P, P, I32P]
+    lib.lora_cache_unload.restype = i32
+    lib.lora_cache_unload.argtypes = [P, i64, I32P]
+    lib.lora_cache_pin.restype = i32
+    lib.lora_cache_pin.argtypes = [P, i64, i32, I32P, I32P, I64P]
+    lib.lora_cache_lookup.restype = i32
+    lib.lora_cache_lookup.argtypes = [P, i64, I32P]
+    lib.lora_cache_slot_table.restype = i32
+    lib.lora_cache_slot_table.argtypes = [P, i32, P, P]
+    lib.lora_write_slot.restype = i32
+    lib.lora_write_slot.argtypes = [D, i32] + [P] * 8 + [P]
+    lib.lora_reset_slot.restype = i32
+    lib.lora_reset_slot.argtypes = [D, i32] + [P] * 4 + [P]
     _lib = lib
     return lib
 
@@ -159,7 +181,7 @@ def lora_status_string(code: int) -> str:
 def _check(code: int, where: str):
     if code != 0:
         name = lora_status_string(code)
-        cls = _LoraValueError if 1 <= code <= 4 else LoraError
+        cls = _LoraValueError if (1 <= code <= 4 or code in (7, 8)) else LoraError
         raise cls(code, name, where)
 
 
@@ -345,3 +367,95 @@ def packed_to_torch(a: np.ndarray):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).copy())
+
+
+# ----------------------------------------------------------------------------- slot cache
+CACHE_LRU, CACHE_NO_EVICT = 0, 1
+
+
+class LoraSlotCache:
+    """Host slot cache (lora_cache_*): which adapter id holds which slot."""
+
+    def __init__(self, num_slots: int, policy: int = CACHE_LRU):
+        self._h = ctypes.c_void_p()
+        _check(_load().lora_cache_create(int(num_slots), int(policy), ctypes.byref(self._h)), "lora_cache_create")
+        self.num_slots = int(num_slots)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.lora_cache_destroy(h)
+            self._h = None
+
+    def activate(self, adapter_id: int) -> Tuple[int, bool, int]:
+        """(slot, needs_load, evicted adapter id or -1)."""
+        s, l, e = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+        _check(_load().lora_cache_activate(self._h, int(adapter_id), ctypes.byref(s), ctypes.byref(l),
+                                           ctypes.byref(e)), "lora_cache_activate")
+        return s.value, bool(l.value), e.value
+
+    def activate_batch(self, adapter_ids) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """(request_slot int32[n], load_slots int32[k], load_ids int64[k])."""
+        ids = np.ascontiguousarray(adapter_ids, np.int64)
+        n = len(ids)
+        rs = np.zeros(max(n, 1), np.int32)
+        ls = np.zeros(max(n, 1), np.int32)
+        li = np.zeros(max(n, 1), np.int64)
+        k = ctypes.c_int32()
+        _check(_load().lora_cache_activate_batch(self._h, n, _np_ptr(ids) if n else None, _np_ptr(rs),
+                                                 _np_ptr(ls), _np_ptr(li), ctypes.byref(k)),
+               "lora_cache_activate_batch")
+        return rs[:n].copy(), ls[:k.value].copy(), li[:k.value].copy()
+
+    def unload(self, adapter_id: int) -> int:
+        s = ctypes.c_int32()
+        _check(_load().lora_cache_unload(self._h, int(adapter_id), ctypes.byref(s)), "lora_cache_unload")
+        return s.value
+
+    def pin(self, adapter_id: int, pinned: bool = True) -> Tuple[int, bool, int]:
+        s, l, e = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+        _check(_load().lora_cache_pin(self._h, int(adapter_id), 1 if pinned else 0, ctypes.byref(s),
+                                      ctypes.byref(l), ctypes.byref(e)), "lora_cache_pin")
+        return s.value, bool(l.value), e.value
+
+    def lookup(self, adapter_id: int) -> int:
+        s = ctypes.c_int32()
+        _check(_load().lora_cache_lookup(self._h, int(adapter_id), ctypes.byref(s)), "lora_cache_lookup")
+        return s.value
+
+    def slot_table(self) -> Tuple[np.ndarray, np.ndarray]:
+        ids = np.zeros(self.num_slots, np.int64)
+        pinned = np.zeros(self.num_slots, np.uint8)
+        _check(_load().lora_cache_slot_table(self._h, self.num_slots, _np_ptr(ids), _np_ptr(pinned)),
+               "lora_cache_slot_table")
+        return ids, pinned
+
+
+def lora_write_slot(dims: LoraDims, slot: int, packed, stacks, stream=None) -> None:
+    """Copy one adapter's packed host tensors (lora_pack_adapter's dict, or
+    host torch tensors with the same keys) into slot `slot` of the four
+    device stacks {"A_qkv", "B_qkv", "A_o", "B_o"}, asynchronously."""
+    keys = ("A_qkv", "B_qkv", "A_o", "B_o")
+    src = []
+    for k in keys:
+        a = packed[k]
+        if isinstance(a, np.ndarray):
+            if not a.flags["C_CONTIGUOUS"]:
+                raise ValueError(f"{k} must be contiguous")
+            src.append(_np_ptr(a))
+        else:
+            if a.is_cuda or not a.is_contiguous():
+                raise ValueError(f"{k} must be a contiguous host tensor")
+            src.append(a.data_ptr())
+    dc = dims.c()
+    _check(_load().lora_write_slot(ctypes.byref(dc), int(slot), *src,
+                                   *[_dev_ptr(stacks[k], k) for k in keys], _stream_handle(stream)),
+           "lora_write_slot")
+
+
+def lora_reset_slot(dims: LoraDims, slot: int, stacks, stream=None) -> None:
+    """Zero slot `slot` of the four device stacks, asynchronously."""
+    keys = ("A_qkv", "B_qkv", "A_o", "B_o")
+    dc = dims.c()
+    _check(_load().lora_reset_slot(ctypes.byref(dc), int(slot), *[_dev_ptr(stacks[k], k) for k in keys],
+                                   _stream_handle(stream)), "lora_reset_slot")

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblora_sgmv.so")
-SOURCES = [os.path.join(CSRC, "lora_sgmv.hip"), os.path.join(CSRC, "lora_host.cpp")]
+SOURCES = [os.path.join(CSRC, "lora_sgmv.hip"), os.path.join(CSRC, "lora_host.cpp"),
+           os.path.join(CSRC, "lora_cache.cpp")]
 ARCH = "gfx950"
 
 

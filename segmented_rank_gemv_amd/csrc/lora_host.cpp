@@ -173,6 +173,8 @@ const char* lora_status_string(lora_status_t s)
     case LORA_ERR_CAPACITY: return "LORA_ERR_CAPACITY";
     case LORA_ERR_DEVICE: return "LORA_ERR_DEVICE";
     case LORA_ERR_UNSPECIFIED: return "LORA_ERR_UNSPECIFIED";
+    case LORA_ERR_NO_FREE_SLOT: return "LORA_ERR_NO_FREE_SLOT";
+    case LORA_ERR_NOT_ACTIVE: return "LORA_ERR_NOT_ACTIVE";
     default: return "LORA_ERR_UNKNOWN";
     }
 }

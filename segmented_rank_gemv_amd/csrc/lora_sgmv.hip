@@ -596,6 +596,14 @@ __global__ __launch_bounds__(kThreads) void reduce_slabs(const float* P, int64_t
     reinterpret_cast<float4*>(u)[i] = acc;
 }
 
+// Zero n 16-byte words (slot reset; a kernel rather than a memset so that
+// it can be recorded in a HIP graph).
+__global__ __launch_bounds__(kThreads) void zero_words(uint4* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // expand
 
@@ -1889,6 +1897,69 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
         S = 1;
     }
     return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, y, ldy, path, s);
+}
+
+// Bytes of one slot of each stack: A_qkv, B_qkv, A_o, B_o.
+static lora_status_t slot_bytes(const lora_dims_t* dims, size_t b[4])
+{
+    FamilyShape q, o;
+    lora_status_t st = family_shape(dims, LORA_FAMILY_QKV, &q);
+    if (st == LORA_OK)
+        st = family_shape(dims, LORA_FAMILY_O, &o);
+    if (st != LORA_OK)
+        return st;
+    b[0] = (size_t)a_tiled_elems(q.C, q.in_f) * q.elem;
+    b[1] = (size_t)q.out_f * q.R * q.elem;
+    b[2] = (size_t)a_tiled_elems(o.C, o.in_f) * o.elem;
+    b[3] = (size_t)o.out_f * o.R * o.elem;
+    return LORA_OK;
+}
+
+lora_status_t lora_write_slot(const lora_dims_t* dims, int32_t slot, const void* A_qkv, const void* B_qkv,
+                              const void* A_o, const void* B_o, void* A_qkv_stack, void* B_qkv_stack,
+                              void* A_o_stack, void* B_o_stack, void* stream)
+{
+    size_t b[4];
+    const lora_status_t st = slot_bytes(dims, b);
+    if (st != LORA_OK)
+        return st;
+    const void* src[4] = {A_qkv, B_qkv, A_o, B_o};
+    void* dst[4] = {A_qkv_stack, B_qkv_stack, A_o_stack, B_o_stack};
+    if (slot < 0 || slot >= dims->max_num_loras)
+        return LORA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 4; ++i)
+        if (!src[i] || !dst[i])
+            return LORA_ERR_INVALID_ARGUMENT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int i = 0; i < 4; ++i)
+        if (hipMemcpyAsync(reinterpret_cast<char*>(dst[i]) + (size_t)slot * b[i], src[i], b[i],
+                           hipMemcpyHostToDevice, s) != hipSuccess)
+            return LORA_ERR_DEVICE;
+    return LORA_OK;
+}
+
+lora_status_t lora_reset_slot(const lora_dims_t* dims, int32_t slot, void* A_qkv_stack, void* B_qkv_stack,
+                              void* A_o_stack, void* B_o_stack, void* stream)
+{
+    size_t b[4];
+    const lora_status_t st = slot_bytes(dims, b);
+    if (st != LORA_OK)
+        return st;
+    void* dst[4] = {A_qkv_stack, B_qkv_stack, A_o_stack, B_o_stack};
+    if (slot < 0 || slot >= dims->max_num_loras)
+        return LORA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 4; ++i)
+        if (!dst[i] || !aligned16(dst[i]))
+            return LORA_ERR_INVALID_ARGUMENT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int i = 0; i < 4; ++i) {
+        // slot sizes are multiples of 16 bytes (widths and ranks are multiples of 8)
+        const int64_t n = (int64_t)(b[i] / 16);
+        const unsigned grid = (unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
+        hipLaunchKernelGGL(zero_words, dim3(grid), dim3(kThreads), 0, s,
+                           reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst[i]) + (size_t)slot * b[i]), n);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
 }  // extern "C"
