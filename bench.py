@@ -46,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-REPLICAS = {"tiny": 1, "decode": 64, "prefill": 2, "mixed": 8, "stack": 32}
+REPLICAS = {"tiny": 1, "decode": 64, "prefill": 2, "mixed": 8, "stack": 32, "mlp": 32}
 KERNEL_SRC = os.path.join(ROOT, "segmented_rank_gemv_amd", "csrc", "lora_sgmv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -165,8 +165,16 @@ def main():
     n_layers = args.layers or REPLICAS[args.workload]
     if args.workload == "stack" and not args.layers:
         n_layers = w.n_layers
+    mlp = w.intermediate > 0
     dims = srg.LoraDims(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank,
-                        w.max_num_loras, w.dtype)
+                        w.max_num_loras, w.dtype, w.intermediate)
+    # projection families of the workload: (family, name, x, y, A stack, B stack, PEFT projections)
+    if mlp:
+        FAMS = ((srg.FAMILY_GATE_UP, "gu", "x_gu", "y_gu", "A_gu", "B_gu", ("gate", "up")),
+                (srg.FAMILY_DOWN, "down", "x_down", "y_down", "A_down", "B_down", ("down",)))
+    else:
+        FAMS = ((srg.FAMILY_QKV, "qkv", "x_qkv", "y_qkv", "A_qkv", "B_qkv", ("q", "k", "v")),
+                (srg.FAMILY_O, "o", "x_o", "y_o", "A_o", "B_o", ("o",)))
     lengths, slots = synth.draw_requests(w)
     ranks = synth.draw_ranks(w)
     offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
@@ -181,7 +189,8 @@ def main():
     rt0 = srg.lora_build_routing(slots, offsets, L)
     end, G = rt0["end"], rt0["num_groups"]
     order = np.concatenate([np.arange(offsets[p], offsets[p + 1]) for p in rt0["perm"]])
-    fam_shape = {f: srg.lora_family_shape(dims, f) for f in (srg.FAMILY_QKV, srg.FAMILY_O)}
+    fam_shape = {fm[0]: srg.lora_family_shape(dims, fm[0]) for fm in FAMS}
+    proj_desc = "gate/up/down" if mlp else "q/k/v/o"
     log(f"workload={w.name} T={T} end={end} G={G} layers={n_layers}")
 
     def to_dev(a):
@@ -196,19 +205,29 @@ def main():
     n_pack = 0
     layers = []
     for l in range(n_layers):
-        st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+        st = {k: [] for fm in FAMS for k in fm[4:6]}
         for s in range(L):
-            wts = synth.draw_adapter(w, l, s, int(ranks[s]))
-            t0 = time.perf_counter()
-            pk = srg.lora_pack_adapter(dims, int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo", wts)
+            if mlp:
+                wts = synth.draw_mlp_adapter(w, l, s, int(ranks[s]))
+                t0 = time.perf_counter()
+                pk = {}
+                for f, nm, xk, yk, ak, bk, projs in FAMS:
+                    r = srg.lora_pack_family(dims, f, int(ranks[s]), w.lora_alpha, w.use_rslora, True,
+                                             [wts[p] for p in projs])
+                    pk[ak], pk[bk] = r["A"], r["B"]
+            else:
+                wts = synth.draw_adapter(w, l, s, int(ranks[s]))
+                t0 = time.perf_counter()
+                pk = srg.lora_pack_adapter(dims, int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo", wts)
             t_pack += time.perf_counter() - t0
             n_pack += 1
             for k in st:
                 st[k].append(pk[k])
-        acts = synth.draw_activations(w, l, T)
+        acts = synth.draw_mlp_activations(w, l, T) if mlp else synth.draw_activations(w, l, T)
         layer = {k: to_dev(np.stack(v)) for k, v in st.items()}
-        for k in ("x_qkv", "y_qkv", "x_o", "y_o"):
-            layer[k] = to_dev(np.ascontiguousarray(acts[k][order]))
+        for fm in FAMS:
+            for k in fm[2:4]:
+                layer[k] = to_dev(np.ascontiguousarray(acts[k][order]))
         layers.append(layer)
         if (l + 1) % 16 == 0:
             log(f"  prepared {l + 1}/{n_layers} layers")
@@ -236,15 +255,14 @@ def main():
         ids_dev.copy_(ids_pin, non_blocking=True)
         offs_dev.copy_(offs_pin, non_blocking=True)
 
-    FAMS = ((srg.FAMILY_QKV, "qkv", "x_qkv", "y_qkv", "A_qkv", "B_qkv"),
-            (srg.FAMILY_O, "o", "x_o", "y_o", "A_o", "B_o"))
     if args.api == "delta":
-        KINDS = ("delta_qkv", "delta_o")
+        KINDS = tuple("delta_" + fm[1] for fm in FAMS)
     else:
-        KINDS = ("shrink_qkv", "expand_qkv", "shrink_o", "expand_o")
+        KINDS = tuple(k + "_" + fm[1] for fm in FAMS for k in ("shrink", "expand"))
+    BY_NAME = {fm[1]: fm for fm in FAMS}
 
     def call(kind, ly):
-        f, nm, xk, yk, ak, bk = FAMS[0] if kind.endswith("_qkv") else FAMS[1]
+        f, nm, xk, yk, ak, bk, _ = BY_NAME[kind.split("_", 1)[1]]
         if kind.startswith("delta"):
             srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path)
         elif kind.startswith("shrink"):
@@ -386,7 +404,7 @@ def main():
     # stream).  Each slot is rewritten with the adapter it already holds, so
     # the stacks are unchanged.
     activation = None
-    if L > 1:
+    if L > 1 and not mlp:
         cache = srg.LoraSlotCache(L)
         crng = np.random.default_rng(5)
         nb, loads = 2000, 0
@@ -438,18 +456,29 @@ def main():
         n_distinct = min(n_layers, 4)
         lora_req = [i for i in range(len(slots)) if slots[i] >= 0]
         # bound the rows per call for the long workloads (about 0.1-1 s each)
-        budget = max(1, int(2e8 // (fam_shape[0][0] * fam_shape[0][1] * R + fam_shape[0][3] * R)))
+        f0 = FAMS[0][0]
+        budget = max(1, int(2e8 // (fam_shape[f0][0] * fam_shape[f0][1] * R + fam_shape[f0][3] * R)))
         while t_cpu < args.cpu_seconds and n_calls < 100000:
             l = n_calls % n_distinct
             if l >= len(prepared):
-                st = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
+                st = {k: [] for fm in FAMS for k in fm[4:6]}
                 for s in range(L):
-                    pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
-                                             int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
-                                             synth.draw_adapter(w, l, s, int(ranks[s])))
+                    if mlp:
+                        wts = synth.draw_mlp_adapter(w, l, s, int(ranks[s]))
+                        pk = {}
+                        for f, nm, xk, yk, ak, bk, projs in FAMS:
+                            fin, _, widths, _ = fam_shape[f]
+                            r = oracle.pack_family(fin, widths, R, w.dtype, int(ranks[s]), w.lora_alpha,
+                                                   w.use_rslora, True, [wts[p] for p in projs])
+                            pk[ak], pk[bk] = r["A"], r["B"]
+                    else:
+                        pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
+                                                 int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
+                                                 synth.draw_adapter(w, l, s, int(ranks[s])))
                     for k in st:
                         st[k].append(pk[k])
-                prepared.append(({k: np.stack(v) for k, v in st.items()}, synth.draw_activations(w, l, T)))
+                acts_l = synth.draw_mlp_activations(w, l, T) if mlp else synth.draw_activations(w, l, T)
+                prepared.append(({k: np.stack(v) for k, v in st.items()}, acts_l))
             st, acts = prepared[l]
             order_req = lora_req[n_calls % len(lora_req):] + lora_req[:n_calls % len(lora_req)]
             rows, left = {}, budget
@@ -459,16 +488,15 @@ def main():
                 left -= len(rows[i])
             reqs = [i for i in order_req if len(rows[i])]
             t0 = time.perf_counter()
-            oracle.reference_family(acts["x_qkv"], acts["y_qkv"], offsets, slots, st["A_qkv"], st["B_qkv"],
-                                    [w.nq, w.nkv, w.nkv], R, w.dtype, reqs, rows)
-            oracle.reference_family(acts["x_o"], acts["y_o"], offsets, slots, st["A_o"], st["B_o"],
-                                    [w.hidden], R, w.dtype, reqs, rows)
+            for f, nm, xk, yk, ak, bk, _ in FAMS:
+                oracle.reference_family(acts[xk], acts[yk], offsets, slots, st[ak], st[bk],
+                                        list(fam_shape[f][2]), R, w.dtype, reqs, rows)
             t_cpu += time.perf_counter() - t0
             tokens_done += sum(len(rows[i]) for i in reqs)
             n_calls += 1
         cpu = {"value": tokens_done / t_cpu, "unit": "LoRA tokens x layers / s", "cores": 1,
                "kind": "oracle",
-               "sample": f"{tokens_done} LoRA-routed token rows through the q/k/v/o delta of one layer "
+               "sample": f"{tokens_done} LoRA-routed token rows through the {proj_desc} delta of one layer "
                          f"({n_calls} oracle passes over {len(prepared)} distinct layers of the same "
                          f"workload, at most {budget} rows per pass), fp64, single thread, {t_cpu:.1f} s"}
         log(f"phase 3: oracle {cpu['value']:.1f} tokens x layers/s")
@@ -476,7 +504,7 @@ def main():
     out = {
         "metric": "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), Llama-8B QKV shape",
         "value": value,
-        "unit": "LoRA tokens x layers / s (q/k/v/o delta)",
+        "unit": f"LoRA tokens x layers / s ({proj_desc} delta)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -487,6 +515,7 @@ def main():
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded; adapters, activations and routing drawn per layer)",
         "config": {"workload": w.name, "hidden": w.hidden, "n_heads": w.n_heads,
+                   "intermediate": w.intermediate if mlp else None,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "requests": int(len(slots)),
                    "tokens": T, "lora_tokens": end, "groups": G, "max_num_loras": L,
                    "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 4
+#define LORA_ABI_VERSION 5
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -67,8 +67,14 @@ enum { LORA_DTYPE_F32 = 0, LORA_DTYPE_BF16 = 1 };
 /* Projection families.  QKV: input width hidden, three output slices of
  * widths (n_heads*head_dim, n_kv_heads*head_dim, n_kv_heads*head_dim).
  * O: input width n_heads*head_dim, one output slice of width hidden.
- * ([MAX-lora] LoRATargetModule: fused self_attn.qkv = (q,k,v)_proj; o_proj.) */
-enum { LORA_FAMILY_QKV = 0, LORA_FAMILY_O = 1 };
+ * ([MAX-lora] LoRATargetModule: fused self_attn.qkv = (q,k,v)_proj; o_proj.)
+ * GATE_UP: input width hidden, two output slices of width intermediate_size
+ * (gate_proj, up_proj fused like q/k/v); DOWN: input width
+ * intermediate_size, one output slice of width hidden (down_proj).  The MLP
+ * families need intermediate_size > 0 ([MAX-lora] 目标模块白名单: the MLP
+ * projections gate_proj/up_proj/down_proj, a TODO there; [vLLM] §5.4 packed
+ * modules). */
+enum { LORA_FAMILY_QKV = 0, LORA_FAMILY_O = 1, LORA_FAMILY_GATE_UP = 2, LORA_FAMILY_DOWN = 3 };
 
 /* Adapter target bits (q_proj, k_proj, v_proj, o_proj). */
 enum { LORA_TARGET_Q = 1, LORA_TARGET_K = 2, LORA_TARGET_V = 4, LORA_TARGET_O = 8 };
@@ -88,8 +94,10 @@ enum { LORA_PATH_AUTO = 0, LORA_PATH_VALU = 1, LORA_PATH_MFMA = 2, LORA_PATH_FUS
 /* Model and LoRA capacity dimensions.  max_lora_rank (R) and max_num_loras (L)
  * correspond to LoRAConfig.max_lora_rank / max_num_loras ([MAX-lora] LoRAConfig
  * table; page defaults 16 and 1).  Constraints checked by every call:
- * all fields > 0; hidden, n_heads*head_dim and n_kv_heads*head_dim multiples
- * of 8 and at most 2^20; max_lora_rank a multiple of 8 and <= 128; dtype one of LORA_DTYPE_*. */
+ * all fields > 0 except intermediate_size; hidden, n_heads*head_dim,
+ * n_kv_heads*head_dim and intermediate_size multiples of 8 and at most 2^20;
+ * max_lora_rank a multiple of 8 and <= 128; dtype one of LORA_DTYPE_*;
+ * intermediate_size 0 when the model's MLP is not targeted. */
 typedef struct lora_dims {
     int32_t hidden;
     int32_t n_heads;
@@ -98,6 +106,7 @@ typedef struct lora_dims {
     int32_t max_lora_rank;
     int32_t max_num_loras;
     int32_t dtype;
+    int32_t intermediate_size;
 } lora_dims_t;
 
 /* Library ABI version (LORA_ABI_VERSION of the build). */
@@ -179,6 +188,22 @@ lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lor
  * A base-only or empty batch gives G = 0, end = 0; the device calls then do
  * nothing.
  */
+/* Host, synchronous: pack one adapter's projections of one family into one
+ * slot's A and B — the steps of lora_pack_adapter (validate, scale B by
+ * alpha/r or alpha/sqrt(r), zero-pad to max_lora_rank, concatenate the
+ * slices, round to the stack dtype) for any family, the MLP ones included.
+ * Slice s (in the family's slice order, e.g. gate then up) takes A_slices[s]
+ * [rank][in_features] and B_slices[s] [width_s][rank] (fp32, PEFT layout)
+ * when bit s of slice_mask is set, and is a zero block otherwise ([vLLM]
+ * §5.3 reset_lora).  A_out: the tiled A layout, round16(n_slices*R) rows;
+ * B_out: [out_features][R].  Errors: INVALID_ARGUMENT (dims, family, NULL
+ * pointers for a set bit), INVALID_ADAPTER (bias not none, rank outside
+ * [1, max_lora_rank], mask bits past the family's slices). */
+lora_status_t lora_pack_family(const lora_dims_t* dims, int32_t family, int32_t rank, float lora_alpha,
+                               int32_t use_rslora, int32_t bias_none, uint32_t slice_mask,
+                               const float* const* A_slices, const float* const* B_slices, void* A_out,
+                               void* B_out);
+
 lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
                                  const int64_t* row_offsets, int32_t max_num_loras,
                                  int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,

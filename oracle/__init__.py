@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     delta,
     library_path,
     pack_adapter,
+    pack_family,
     reference_family,
     route,
     scaling,

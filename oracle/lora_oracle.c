@@ -196,6 +196,66 @@ int oracle_pack_adapter(int32_t hidden, int32_t n_heads, int32_t n_kv_heads, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Packing of any projection family (the MLP ones included): the same five
+ * steps as oracle_pack_adapter — validate, pre-multiply the scale into B in
+ * fp32, zero-pad to max_rank, concatenate the slices (A along the rank dim,
+ * B along the output dim), cast — for n_slices slices of widths[s] over
+ * input width in_f.  Slice s is present when bit s of slice_mask is set
+ * ([MAX-lora] 加载时的处理管线 for the steps; [vLLM] §5.4 packed modules for
+ * fusing projections that share an input, as gate_proj/up_proj do).
+ * Outputs (row-major, dtype `dtype`): A [n_slices R][in_f], B [sum widths][R].
+ */
+int oracle_pack_family(int32_t in_f, int32_t n_slices, const int32_t* widths, int32_t max_rank, int32_t dtype,
+                       int32_t r, double alpha, int32_t use_rslora, int32_t bias_none, uint32_t slice_mask,
+                       const float* const* A_in, const float* const* B_in, void* A_out, void* B_out)
+{
+    if (in_f <= 0 || n_slices <= 0 || n_slices > 4 || !widths || max_rank <= 0)
+        return OR_BAD_ARG;
+    if (dtype != OR_DTYPE_F32 && dtype != OR_DTYPE_BF16)
+        return OR_BAD_ARG;
+    if (!A_out || !B_out || !A_in || !B_in)
+        return OR_BAD_ARG;
+    /* step 1: validation */
+    if (!bias_none || r < 1 || r > max_rank || (slice_mask >> n_slices))
+        return OR_BAD_ADAPTER;
+    for (int s = 0; s < n_slices; ++s)
+        if (((slice_mask >> s) & 1u) && (!A_in[s] || !B_in[s]))
+            return OR_BAD_ARG;
+    const int64_t R = max_rank;
+    int64_t n_out = 0;
+    for (int s = 0; s < n_slices; ++s)
+        n_out += widths[s];
+    const float scale = (float)oracle_scaling(alpha, r, use_rslora);
+    float* A_cat = (float*)calloc((size_t)(n_slices * R * in_f), sizeof(float));
+    float* B_cat = (float*)calloc((size_t)(n_out * R), sizeof(float));
+    int64_t brow = 0;
+    for (int s = 0; s < n_slices; ++s) {
+        if ((slice_mask >> s) & 1u) {
+            /* steps 3 and 4: rows [s R, s R + r) of A, columns [0, r) of B */
+            for (int64_t i = 0; i < r; ++i)
+                for (int64_t k = 0; k < in_f; ++k)
+                    A_cat[(s * R + i) * in_f + k] = A_in[s][i * in_f + k];
+            /* step 2: B times the scale in fp32 */
+            for (int64_t o = 0; o < widths[s]; ++o)
+                for (int64_t j = 0; j < r; ++j)
+                    B_cat[(brow + o) * R + j] = B_in[s][o * r + j] * scale;
+        }
+        brow += widths[s];
+    }
+    /* step 5: cast */
+    if (dtype == OR_DTYPE_F32) {
+        memcpy(A_out, A_cat, sizeof(float) * (size_t)(n_slices * R * in_f));
+        memcpy(B_out, B_cat, sizeof(float) * (size_t)(n_out * R));
+    } else {
+        oracle_bf16_round_array(A_cat, (uint16_t*)A_out, n_slices * R * in_f);
+        oracle_bf16_round_array(B_cat, (uint16_t*)B_out, n_out * R);
+    }
+    free(A_cat);
+    free(B_cat);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batch routing.
  *
  * [MAX-V3] sort_lora_batch(): same-adapter requests adjacent, ordered by

@@ -65,6 +65,8 @@ def _load():
     lib.oracle_pack_adapter.restype = i32
     lib.oracle_pack_adapter.argtypes = [i32, i32, i32, i32, i32, i32, i32, f64, i32, i32, u32,
                                         P, P, P, P, P, P]
+    lib.oracle_pack_family.restype = i32
+    lib.oracle_pack_family.argtypes = [i32, i32, P, i32, i32, i32, f64, i32, i32, u32, P, P, P, P]
     lib.oracle_route.restype = i32
     lib.oracle_route.argtypes = [i32, P, P, i32, P, P, P, P, P, P]
     lib.oracle_delta.restype = i32
@@ -141,6 +143,37 @@ def pack_adapter(hidden: int, n_heads: int, n_kv_heads: int, head_dim: int, max_
                                    _ptr(out["B_o"]))
     if code != 0:
         raise OracleError(code, "pack")
+    return out
+
+
+def pack_family(in_f: int, widths: Sequence[int], max_rank: int, dtype: str, rank: int, alpha: float,
+                use_rslora: bool, bias_none: bool,
+                slices: Sequence[Optional[Tuple[np.ndarray, np.ndarray]]]) -> Dict[str, np.ndarray]:
+    """Pack one adapter's slices of one family: {"A" [n_s R, in_f], "B" [sum widths, R]}
+    in the stack dtype (logical layout)."""
+    lib = _load()
+    n_s = len(widths)
+    R = max_rank
+    st = np.uint16 if dtype == "bf16" else np.float32
+    out = {"A": np.zeros((n_s * R, in_f), dtype=st), "B": np.zeros((int(sum(widths)), R), dtype=st)}
+    keep, mask = [], 0
+    a_ptrs = (ctypes.c_void_p * n_s)()
+    b_ptrs = (ctypes.c_void_p * n_s)()
+    for i, sl in enumerate(slices):
+        if sl is None:
+            continue
+        a = np.ascontiguousarray(sl[0], dtype=np.float32)
+        b = np.ascontiguousarray(sl[1], dtype=np.float32)
+        keep += [a, b]
+        a_ptrs[i], b_ptrs[i] = _ptr(a), _ptr(b)
+        mask |= 1 << i
+    w = np.ascontiguousarray(widths, dtype=np.int32)
+    code = lib.oracle_pack_family(int(in_f), n_s, _ptr(w), R, DTYPE_CODE[dtype], int(rank), float(alpha),
+                                  int(bool(use_rslora)), int(bool(bias_none)), mask,
+                                  ctypes.cast(a_ptrs, ctypes.c_void_p), ctypes.cast(b_ptrs, ctypes.c_void_p),
+                                  _ptr(out["A"]), _ptr(out["B"]))
+    if code != 0:
+        raise OracleError(code, "pack_family")
     return out
 
 

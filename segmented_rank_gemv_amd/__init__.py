@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     lora_write_slot,
     DTYPE_BF16,
     DTYPE_F32,
+    FAMILY_DOWN,
+    FAMILY_GATE_UP,
     FAMILY_O,
     FAMILY_QKV,
     PATH_AUTO,
@@ -34,6 +36,7 @@ from ._lib import (  # noqa: F401
     lora_build_routing,
     lora_family_shape,
     lora_pack_adapter,
+    lora_pack_family,
     lora_sgmv_delta,
     lora_sgmv_expand,
     lora_sgmv_shrink,

@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "liblora_sgmv.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-FAMILY_QKV, FAMILY_O = 0, 1
+FAMILY_QKV, FAMILY_O, FAMILY_GATE_UP, FAMILY_DOWN = 0, 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_FUSED = 0, 1, 2, 3
 _TARGET_BITS = {"q": 1, "k": 2, "v": 4, "o": 8}
 _DTYPES = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
@@ -38,7 +38,7 @@ class _LoraDims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_lora_rank", ctypes.c_int32), ("max_num_loras", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("intermediate_size", ctypes.c_int32)]
 
 
 class _LoraRouting(ctypes.Structure):
@@ -105,10 +105,12 @@ class LoraDims:
     max_lora_rank: int = 16
     max_num_loras: int = 1
     dtype: str = "bf16"
+    intermediate_size: int = 0  # MLP width; 0 = MLP not targeted
 
     def c(self) -> _LoraDims:
         return _LoraDims(self.hidden, self.n_heads, self.n_kv_heads, self.head_dim,
-                         self.max_lora_rank, self.max_num_loras, _DTYPES[self.dtype])
+                         self.max_lora_rank, self.max_num_loras, _DTYPES[self.dtype],
+                         self.intermediate_size)
 
 
 def library_path() -> str:
@@ -138,6 +140,8 @@ def _load():
     lib.lora_family_shape.argtypes = [D, i32, P, P, P, P]
     lib.lora_pack_adapter.restype = i32
     lib.lora_pack_adapter.argtypes = [D, i32, ctypes.c_float, i32, i32, u32] + [P] * 12
+    lib.lora_pack_family.restype = i32
+    lib.lora_pack_family.argtypes = [D, i32, i32, ctypes.c_float, i32, i32, u32, P, P, P, P]
     lib.lora_build_routing.restype = i32
     lib.lora_build_routing.argtypes = [i32, P, P, i32, P, P, P, P, P, P]
     lib.lora_sgmv_workspace_bytes.restype = i32
@@ -267,6 +271,38 @@ def lora_pack_adapter(dims: LoraDims, rank: int, lora_alpha: float, use_rslora: 
                                      *ptrs, _np_ptr(out["A_qkv"]), _np_ptr(out["B_qkv"]),
                                      _np_ptr(out["A_o"]), _np_ptr(out["B_o"])),
            "lora_pack_adapter")
+    return out
+
+
+def lora_pack_family(dims: LoraDims, family: int, rank: int, lora_alpha: float, use_rslora: bool,
+                     bias_none: bool, slices: Sequence[Optional[Tuple[np.ndarray, np.ndarray]]]
+                     ) -> Dict[str, np.ndarray]:
+    """Pack one adapter's projections of one family: slices[s] = (lora_A
+    [rank, in], lora_B [width_s, rank]) in the family's slice order, or None
+    for an untargeted slice.  Returns {"A": tiled A, "B": [out, R]}."""
+    in_f, n_s, widths, out_f = lora_family_shape(dims, family)
+    if len(slices) != n_s:
+        raise ValueError(f"family {family} has {n_s} slices")
+    R = dims.max_lora_rank
+    st = np.uint16 if dims.dtype == "bf16" else np.float32
+    out = {"A": np.empty(a_tiled_shape(n_s * R, in_f), st), "B": np.empty((out_f, R), st)}
+    keep, mask = [], 0
+    a_ptrs = (ctypes.c_void_p * max(n_s, 1))()
+    b_ptrs = (ctypes.c_void_p * max(n_s, 1))()
+    for i, sl in enumerate(slices):
+        if sl is None:
+            continue
+        a = np.ascontiguousarray(sl[0], dtype=np.float32)
+        b = np.ascontiguousarray(sl[1], dtype=np.float32)
+        keep += [a, b]
+        a_ptrs[i], b_ptrs[i] = _np_ptr(a), _np_ptr(b)
+        mask |= 1 << i
+    dc = dims.c()
+    _check(_load().lora_pack_family(ctypes.byref(dc), int(family), int(rank), float(lora_alpha),
+                                    int(bool(use_rslora)), int(bool(bias_none)), mask,
+                                    ctypes.cast(a_ptrs, ctypes.c_void_p), ctypes.cast(b_ptrs, ctypes.c_void_p),
+                                    _np_ptr(out["A"]), _np_ptr(out["B"])),
+           "lora_pack_family")
     return out
 
 

@@ -36,6 +36,8 @@ lora_status_t check_dims(const lora_dims_t* d)
         return LORA_ERR_INVALID_ARGUMENT;
     if (d->max_lora_rank % 8 || d->max_lora_rank > kMaxRank)
         return LORA_ERR_INVALID_ARGUMENT;
+    if (d->intermediate_size < 0 || d->intermediate_size % 8 || d->intermediate_size > kMaxWidth)
+        return LORA_ERR_INVALID_ARGUMENT;
     return LORA_OK;
 }
 
@@ -56,6 +58,15 @@ lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs
         f.widths[2] = nkv;
     } else if (family == LORA_FAMILY_O) {
         f.in_f = nq;
+        f.n_s = 1;
+        f.widths[0] = d->hidden;
+    } else if (family == LORA_FAMILY_GATE_UP && d->intermediate_size > 0) {
+        f.in_f = d->hidden;
+        f.n_s = 2;
+        f.widths[0] = d->intermediate_size;
+        f.widths[1] = d->intermediate_size;
+    } else if (family == LORA_FAMILY_DOWN && d->intermediate_size > 0) {
+        f.in_f = d->intermediate_size;
         f.n_s = 1;
         f.widths[0] = d->hidden;
     } else {
@@ -268,6 +279,56 @@ lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lor
                     ((uint16_t*)B_dst[p])[row * R + j] = to_bf16(v);
                 else
                     ((float*)B_dst[p])[row * R + j] = v;
+            }
+        }
+    }
+    return LORA_OK;
+}
+
+lora_status_t lora_pack_family(const lora_dims_t* dims, int32_t family, int32_t rank, float lora_alpha,
+                               int32_t use_rslora, int32_t bias_none, uint32_t slice_mask,
+                               const float* const* A_slices, const float* const* B_slices, void* A_out,
+                               void* B_out)
+{
+    FamilyShape fs;
+    lora_status_t st = family_shape(dims, family, &fs);
+    if (st != LORA_OK)
+        return st;
+    if (!A_out || !B_out)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (!bias_none || rank < 1 || rank > dims->max_lora_rank || (slice_mask >> fs.n_s))
+        return LORA_ERR_INVALID_ADAPTER;
+    if (!(lora_alpha == lora_alpha))
+        return LORA_ERR_INVALID_ARGUMENT;
+    for (int s = 0; s < fs.n_s; ++s)
+        if (((slice_mask >> s) & 1u) && (!A_slices || !B_slices || !A_slices[s] || !B_slices[s]))
+            return LORA_ERR_INVALID_ARGUMENT;
+    const int64_t R = fs.R, r = rank, K = fs.in_f;
+    const double scale = use_rslora ? (double)lora_alpha / sqrt((double)rank) : (double)lora_alpha / (double)rank;
+    const float scale32 = (float)scale;
+    const bool bf16 = fs.elem == 2;
+    memset(A_out, 0, (size_t)a_tiled_elems(fs.C, K) * fs.elem);
+    for (int s = 0; s < fs.n_s; ++s) {
+        const bool on = (slice_mask >> s) & 1u;
+        // A rows [s R, s R + R) in the tiled layout; rows >= rank are zero
+        for (int64_t i = 0; i < R; ++i)
+            for (int64_t k = 0; k < K; ++k) {
+                const float v = (on && i < r) ? A_slices[s][i * K + k] : 0.0f;
+                const int64_t at = a_tiled_index(s * R + i, k, K);
+                if (bf16)
+                    ((uint16_t*)A_out)[at] = to_bf16(v);
+                else
+                    ((float*)A_out)[at] = v;
+            }
+        // B rows [offs[s], offs[s] + width) of width R; columns >= rank are zero
+        for (int64_t o = 0; o < fs.widths[s]; ++o) {
+            const int64_t row = fs.offs[s] + o;
+            for (int64_t j = 0; j < R; ++j) {
+                const float v = (on && j < r) ? B_slices[s][o * r + j] * scale32 : 0.0f;
+                if (bf16)
+                    ((uint16_t*)B_out)[row * R + j] = to_bf16(v);
+                else
+                    ((float*)B_out)[row * R + j] = v;
             }
         }
     }

@@ -16,12 +16,15 @@ is exactly a bf16 value and both sides read identical numbers.
 """
 
 from .workloads import (  # noqa: F401
+    MLP_PROJECTIONS,
     PROJECTIONS,
     WORKLOADS,
     Workload,
     bf16_bits,
     draw_activations,
     draw_adapter,
+    draw_mlp_activations,
+    draw_mlp_adapter,
     draw_ranks,
     draw_requests,
     get_workload,

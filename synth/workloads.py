@@ -16,9 +16,10 @@ from typing import Dict, Tuple
 import numpy as np
 
 PROJECTIONS = ("q", "k", "v", "o")
+MLP_PROJECTIONS = ("gate", "up", "down")
 
 # stream ids of the counter-addressed generators
-_S_REQ, _S_RANK, _S_ADAPTER, _S_ACT = 1, 2, 3, 4
+_S_REQ, _S_RANK, _S_ADAPTER, _S_ACT, _S_MLP_ADAPTER, _S_MLP_ACT = 1, 2, 3, 4, 5, 6
 
 B_VARIANCE = 0.02
 
@@ -38,6 +39,7 @@ class Workload:
     lora_alpha: float
     use_rslora: bool
     seed: int
+    intermediate: int = 0  # MLP width (gate/up output, down input); 0 = attention only
 
     @property
     def nq(self) -> int:
@@ -57,6 +59,10 @@ class Workload:
             return self.hidden, self.nq
         if p in ("k", "v"):
             return self.hidden, self.nkv
+        if p in ("gate", "up"):
+            return self.hidden, self.intermediate
+        if p == "down":
+            return self.intermediate, self.hidden
         if p == "o":
             return self.nq, self.hidden
         raise KeyError(p)
@@ -81,6 +87,10 @@ WORKLOADS: Dict[str, Workload] = {
                  hidden=5120, n_heads=40, n_kv_heads=8, head_dim=128, max_lora_rank=64,
                  max_num_loras=32, dtype="bf16", n_layers=1, lora_alpha=16.0, use_rslora=False,
                  seed=1004),
+        Workload("mlp", "Llama-3-8B MLP (4096 -> 2 x 14336 -> 4096), 256 one-token requests, 8 slots, ranks 8/16, 25% base",
+                 hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, max_lora_rank=16,
+                 max_num_loras=8, dtype="bf16", n_layers=1, lora_alpha=16.0, use_rslora=False,
+                 seed=1006, intermediate=14336),
         Workload("stack", "32-layer Llama-3-8B attention, 4096 tokens in 32 requests, 16 slots, rsLoRA r=32",
                  hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, max_lora_rank=32,
                  max_num_loras=16, dtype="bf16", n_layers=32, lora_alpha=16.0, use_rslora=True,
@@ -117,7 +127,7 @@ def draw_requests(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
     if w.name == "tiny":
         lengths = np.array([5, 3, 4], dtype=np.int64)
         slots = np.array([0, 1, -1], dtype=np.int32)
-    elif w.name == "decode":
+    elif w.name in ("decode", "mlp"):
         n = 256
         lengths = np.ones(n, dtype=np.int64)
         slots = rng.integers(0, L, size=n).astype(np.int32)
@@ -149,7 +159,7 @@ def draw_ranks(w: Workload) -> np.ndarray:
     """Adapter rank of each slot (int32[max_num_loras])."""
     rng = _rng(w, _S_RANK)
     L = w.max_num_loras
-    if w.name == "decode":
+    if w.name in ("decode", "mlp"):
         return rng.choice(np.array([8, 16]), size=L).astype(np.int32)
     if w.name == "mixed":
         return rng.choice(np.array([8, 16, 32, 64]), size=L).astype(np.int32)
@@ -202,3 +212,32 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     if np.any(u & np.uint32(0xFFFF)):
         raise ValueError("values are not exactly representable in bf16")
     return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def draw_mlp_adapter(w: Workload, layer: int, slot: int, rank: int) -> Dict[str, Tuple[np.ndarray, np.ndarray]]:
+    """Unscaled fp32 PEFT matrices of one adapter's MLP projections in one
+    layer: {p: (lora_A [rank, in_p], lora_B [out_p, rank])} for p in gate, up, down."""
+    if w.intermediate <= 0:
+        raise ValueError("workload has no MLP")
+    rng = _rng(w, _S_MLP_ADAPTER, layer, slot)
+    out = {}
+    for p in MLP_PROJECTIONS:
+        fin, fout = w.proj_shape(p)
+        a = rng.standard_normal((rank, fin), dtype=np.float32) * np.float32(1.0 / np.sqrt(fin))
+        b = rng.standard_normal((fout, rank), dtype=np.float32) * np.float32(np.sqrt(B_VARIANCE))
+        out[p] = (a.astype(np.float32), b.astype(np.float32))
+    return out
+
+
+def draw_mlp_activations(w: Workload, layer: int, n_tokens: int) -> Dict[str, np.ndarray]:
+    """x and base y of the two MLP families, tokens in arrival order:
+    x_gu [T, hidden], y_gu [T, 2 intermediate], x_down [T, intermediate], y_down [T, hidden]."""
+    rng = _rng(w, _S_MLP_ACT, layer)
+    shapes = {
+        "x_gu": (n_tokens, w.hidden),
+        "y_gu": (n_tokens, 2 * w.intermediate),
+        "x_down": (n_tokens, w.intermediate),
+        "y_down": (n_tokens, w.hidden),
+    }
+    return {k: _to_dtype_values(rng.standard_normal(s, dtype=np.float32), w.dtype)
+            for k, s in shapes.items()}
