@@ -62,6 +62,7 @@ def parse():
     p.add_argument("--api", default="delta", choices=["delta", "split"],
                    help="delta: lora_sgmv_delta per family; split: lora_sgmv_shrink + lora_sgmv_expand")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--bias", action="store_true", help="every adapter also carries a LoRA bias per projection")
     p.add_argument("--device-routing", action="store_true",
                    help="kernels read the routing from device memory only (no host copies)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -219,6 +220,11 @@ def main():
                 wts = synth.draw_adapter(w, l, s, int(ranks[s]))
                 t0 = time.perf_counter()
                 pk = srg.lora_pack_adapter(dims, int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo", wts)
+            if args.bias:
+                bias = synth.draw_bias(w, l, s, tuple(p for fm in FAMS for p in fm[6]))
+                for f, nm, xk, yk, ak, bk, projs in FAMS:
+                    pk["bias_" + nm] = srg.lora_pack_bias(dims, f, [bias[p] for p in projs])
+                    st.setdefault("bias_" + nm, [])
             t_pack += time.perf_counter() - t0
             n_pack += 1
             for k in st:
@@ -263,12 +269,13 @@ def main():
 
     def call(kind, ly):
         f, nm, xk, yk, ak, bk, _ = BY_NAME[kind.split("_", 1)[1]]
+        bias = ly.get("bias_" + nm)
         if kind.startswith("delta"):
-            srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path)
+            srg.lora_sgmv_delta(dims, f, ly[xk], ly[ak], ly[bk], routing, ly[yk], ws[f], path, bias=bias)
         elif kind.startswith("shrink"):
             srg.lora_sgmv_shrink(dims, f, ly[xk], ly[ak], routing, u[f], ws[f], path)
         else:
-            srg.lora_sgmv_expand(dims, f, u[f], ly[bk], routing, ly[yk], path)
+            srg.lora_sgmv_expand(dims, f, u[f], ly[bk], routing, ly[yk], path, bias=bias)
 
     def layer_pass(ly):
         for kind in KINDS:
@@ -373,6 +380,8 @@ def main():
         C = n_s * R
         x_b, a_b = end * fin * b, G * C * fin * b
         b_b, y_b = G * fout * R * b, 2 * end * fout * b
+        if args.bias:
+            b_b += G * fout * b  # the groups' bias rows
         u_b = end * C * 4
         kbytes["shrink_" + nm] = x_b + a_b + u_b
         kbytes["expand_" + nm] = u_b + b_b + y_b
@@ -389,7 +398,7 @@ def main():
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         key = f"{w.name}:{dominant}"
-        if tr.get("kernel_sha") == kernel_sha() and key in tr.get("kernels", {}):
+        if not args.bias and tr.get("kernel_sha") == kernel_sha() and key in tr.get("kernels", {}):
             traffic = tr["kernels"][key]["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -475,6 +484,12 @@ def main():
                         pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, R, w.dtype,
                                                  int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
                                                  synth.draw_adapter(w, l, s, int(ranks[s])))
+                    if args.bias:
+                        bias = synth.draw_bias(w, l, s, tuple(p for fm in FAMS for p in fm[6]))
+                        for f, nm, xk, yk, ak, bk, projs in FAMS:
+                            pk["bias_" + nm] = oracle.pack_bias(list(fam_shape[f][2]), w.dtype,
+                                                                [bias[p] for p in projs])
+                            st.setdefault("bias_" + nm, [])
                     for k in st:
                         st[k].append(pk[k])
                 acts_l = synth.draw_mlp_activations(w, l, T) if mlp else synth.draw_activations(w, l, T)
@@ -490,7 +505,7 @@ def main():
             t0 = time.perf_counter()
             for f, nm, xk, yk, ak, bk, _ in FAMS:
                 oracle.reference_family(acts[xk], acts[yk], offsets, slots, st[ak], st[bk],
-                                        list(fam_shape[f][2]), R, w.dtype, reqs, rows)
+                                        list(fam_shape[f][2]), R, w.dtype, reqs, rows, st.get("bias_" + nm))
             t_cpu += time.perf_counter() - t0
             tokens_done += sum(len(rows[i]) for i in reqs)
             n_calls += 1
@@ -520,7 +535,7 @@ def main():
                    "tokens": T, "lora_tokens": end, "groups": G, "max_num_loras": L,
                    "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,
                    "api": args.api, "routing": "device" if args.device_routing else "host+device",
-                   "hip_graph": graph is not None},
+                   "hip_graph": graph is not None, "lora_bias": bool(args.bias)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
                      "algorithmic_bytes_per_launch": kbytes[dominant],

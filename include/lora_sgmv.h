@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 5
+#define LORA_ABI_VERSION 6
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -204,6 +204,18 @@ lora_status_t lora_pack_family(const lora_dims_t* dims, int32_t family, int32_t 
                                const float* const* A_slices, const float* const* B_slices, void* A_out,
                                void* B_out);
 
+/* Host, synchronous: pack one adapter's LoRA bias of one family into one
+ * slot of a bias stack [L][out_features].  [vLLM] §5.3 activate_adapter
+ * writes the bias into the slot next to A and B, and only B carries the
+ * scaling (§5.3 optimize); [MAX-lora] LoRAType BIAS names it a bias attached
+ * to B.  The bias is therefore stored as given: bias_out = round(b) in the
+ * stack dtype; slice s (bias_slices[s], width_s fp32) is zero when bit s of
+ * slice_mask is clear (the slot's reset_lora for a module without one).
+ * Errors: INVALID_ARGUMENT (dims, family, NULL output or a NULL slice for a
+ * set bit), INVALID_ADAPTER (mask bits past the family's slices). */
+lora_status_t lora_pack_bias(const lora_dims_t* dims, int32_t family, uint32_t slice_mask,
+                             const float* const* bias_slices, void* bias_out);
+
 lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
                                  const int64_t* row_offsets, int32_t max_num_loras,
                                  int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,
@@ -291,14 +303,18 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
  *
  * u        fp32 [end][n_slices*R] (device), as lora_sgmv_shrink wrote it.
  * B_stack  [L][out_features][R] in dims->dtype.
+ * bias_stack  NULL, or [L][out_features] in dims->dtype (lora_pack_bias): the
+ *          slot's bias is added to the rows of its segments inside the same
+ *          fp32 accumulation as B.u ([MAX-lora] LoRAType BIAS; [vLLM] §5.3
+ *          set_lora's bias, §8 --enable-lora-bias).  16-byte aligned.
  * routing  see lora_routing_t.
  * y        [>= end rows][out_features] in dims->dtype, row stride ldy, updated in place.
  * Alignment: u, B_stack and y 16-byte aligned; ldy*element size a multiple of 16
  * and at most 2^24 bytes.  u must not alias y.
  */
 lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
-                               const void* B_stack, const lora_routing_t* routing, void* y,
-                               int64_t ldy, int32_t path, void* stream);
+                               const void* B_stack, const void* bias_stack, const lora_routing_t* routing,
+                               void* y, int64_t ldy, int32_t path, void* stream);
 
 /* ---------------------------------------------------------------------------
  * lora_sgmv_delta — device, asynchronous on `stream`.
@@ -312,15 +328,15 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  *                     + sum_j B[slot][off_s + o][j] * sum_k A[slot][s*R + j][k] * x[t][k])
  * for t < end, fp32 accumulation, one rounding to dims->dtype.  Rows >= end
  * are neither read nor written.  Arguments as for lora_sgmv_shrink and
- * lora_sgmv_expand; workspace >= lora_sgmv_workspace_bytes(dims, family, end)
+ * lora_sgmv_expand (bias_stack as there); workspace >= lora_sgmv_workspace_bytes(dims, family, end)
  * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
  * path: any LORA_PATH_*; with the one-kernel path (FUSED, or AUTO on short
  * groups) the workspace is not touched and y must not alias x or the stacks.
  */
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                              const void* A_stack, const void* B_stack, const lora_routing_t* routing,
-                              void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
-                              int32_t path, void* stream);
+                              const void* A_stack, const void* B_stack, const void* bias_stack,
+                              const lora_routing_t* routing, void* y, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, int32_t path, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Adapter slot cache — host, synchronous.

@@ -14,8 +14,10 @@ from .oracle import (  # noqa: F401
     library_path,
     pack_adapter,
     pack_family,
+    pack_bias,
     reference_family,
     route,
     scaling,
+    stack_to_f64,
 )
 from .slot_cache import OracleSlotCache, SlotCacheError  # noqa: F401,E402

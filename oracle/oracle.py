@@ -177,6 +177,25 @@ def pack_family(in_f: int, widths: Sequence[int], max_rank: int, dtype: str, ran
     return out
 
 
+def pack_bias(widths: Sequence[int], dtype: str, slices: Sequence[Optional[np.ndarray]]) -> np.ndarray:
+    """One adapter's LoRA bias of one family, [sum widths] in the stack dtype.
+
+    [vLLM] "vLLM LoRA 实现深度解析" §5.3 activate_adapter: set_lora receives
+    the bias beside A and B, and the scaling is folded into B alone
+    (optimize); [MAX-lora] LoRAType BIAS: a bias attached to B.  So the bias
+    is the slices' biases concatenated in slice order (the same order as B's
+    rows, [MAX-lora] QKV fusion), zero for a slice the adapter has none for,
+    cast to the stack dtype.
+    """
+    if len(slices) != len(widths):
+        raise OracleError(1, "pack_bias")
+    parts = []
+    for w, b in zip(widths, slices):
+        parts.append(np.zeros(int(w)) if b is None else np.asarray(b, dtype=np.float32).reshape(int(w)))
+    cat = np.concatenate(parts).astype(np.float32) if parts else np.zeros(0, np.float32)
+    return bf16_round(cat) if dtype == "bf16" else cat
+
+
 def route(slots: np.ndarray, row_offsets: np.ndarray, max_num_loras: int) -> Dict[str, object]:
     lib = _load()
     slots = np.ascontiguousarray(slots, dtype=np.int32)
@@ -225,14 +244,17 @@ def delta(x: np.ndarray, A: np.ndarray, B: np.ndarray, y_in: np.ndarray,
 def reference_family(x: np.ndarray, y_in: np.ndarray, row_offsets: np.ndarray, slots: np.ndarray,
                      A_stack: np.ndarray, B_stack: np.ndarray, widths: Sequence[int], R: int,
                      dtype: str, requests: Optional[Sequence[int]] = None,
-                     token_rows: Optional[Dict[int, np.ndarray]] = None):
+                     token_rows: Optional[Dict[int, np.ndarray]] = None,
+                     bias_stack: Optional[np.ndarray] = None):
     """Reference (y_ref fp64, u fp64) for one projection family of a batch.
 
     x, y_in are float arrays in arrival order ([T, in], [T, out]); A_stack,
     B_stack are the packed stacks [L, ...] in the stack dtype.  Each LoRA
-    request gets y_in + B[slot] (A[slot] x) token by token; base requests get
-    y_in unchanged.  `requests` restricts the work to some requests and
-    `token_rows` to some rows of each (rows relative to the request).
+    request gets y_in + B[slot] (A[slot] x) token by token, plus
+    bias_stack[slot] when a bias stack [L, out] is given (the LoRA layer's
+    bias, [vLLM] §5.3 set_lora); base requests get y_in unchanged.
+    `requests` restricts the work to some requests and `token_rows` to some
+    rows of each (rows relative to the request).
     Returns dicts keyed by request index: {i: (rows, y_ref, u or None)}.
     """
     out = {}
@@ -251,5 +273,7 @@ def reference_family(x: np.ndarray, y_in: np.ndarray, row_offsets: np.ndarray, s
             cache[s] = (stack_to_f64(A_stack[s], dtype), stack_to_f64(B_stack[s], dtype))
         Af, Bf = cache[s]
         u, y = delta(np.asarray(x[a + rows], dtype=np.float64), Af, Bf, yi, widths, R)
+        if bias_stack is not None:
+            y = y + stack_to_f64(bias_stack[s], dtype)[None, :]
         out[i] = (rows, y, u)
     return out

@@ -37,6 +37,7 @@ from ._lib import (  # noqa: F401
     lora_family_shape,
     lora_pack_adapter,
     lora_pack_family,
+    lora_pack_bias,
     lora_sgmv_delta,
     lora_sgmv_expand,
     lora_sgmv_shrink,

@@ -150,9 +150,11 @@ def _load():
     lib.lora_sgmv_shrink.restype = i32
     lib.lora_sgmv_shrink.argtypes = [D, i32, P, i64, P, RT, P, P, ctypes.c_size_t, i32, P]
     lib.lora_sgmv_expand.restype = i32
-    lib.lora_sgmv_expand.argtypes = [D, i32, P, P, RT, P, i64, i32, P]
+    lib.lora_sgmv_expand.argtypes = [D, i32, P, P, P, RT, P, i64, i32, P]
     lib.lora_sgmv_delta.restype = i32
-    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, RT, P, i64, P, ctypes.c_size_t, i32, P]
+    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, RT, P, i64, P, ctypes.c_size_t, i32, P]
+    lib.lora_pack_bias.restype = i32
+    lib.lora_pack_bias.argtypes = [D, i32, u32, P, P]
     I32P, I64P = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.lora_cache_create.restype = i32
     lib.lora_cache_create.argtypes = [i32, i32, ctypes.POINTER(P)]
@@ -306,6 +308,33 @@ def lora_pack_family(dims: LoraDims, family: int, rank: int, lora_alpha: float, 
     return out
 
 
+def lora_pack_bias(dims: LoraDims, family: int, slices: Sequence[Optional[np.ndarray]]) -> np.ndarray:
+    """Pack one adapter's LoRA bias of one family: slices[s] = bias [width_s]
+    in the family's slice order, or None (zero).  Stored as given (only B
+    carries the scaling); returns [out] in the stack dtype (uint16 bf16
+    patterns or float32)."""
+    in_f, n_s, widths, out_f = lora_family_shape(dims, family)
+    if len(slices) != n_s:
+        raise ValueError(f"family {family} has {n_s} slices")
+    st = np.uint16 if dims.dtype == "bf16" else np.float32
+    out = np.empty(out_f, st)
+    keep, mask = [], 0
+    ptrs = (ctypes.c_void_p * max(n_s, 1))()
+    for i, b in enumerate(slices):
+        if b is None:
+            continue
+        b = np.ascontiguousarray(b, dtype=np.float32).reshape(-1)
+        if b.size != widths[i]:
+            raise ValueError(f"bias slice {i} must have {widths[i]} entries")
+        keep.append(b)
+        ptrs[i] = _np_ptr(b)
+        mask |= 1 << i
+    dc = dims.c()
+    _check(_load().lora_pack_bias(ctypes.byref(dc), int(family), mask, ctypes.cast(ptrs, ctypes.c_void_p),
+                                  _np_ptr(out)), "lora_pack_bias")
+    return out
+
+
 def lora_build_routing(request_slot: np.ndarray, row_offsets: np.ndarray,
                        max_num_loras: int) -> Dict[str, object]:
     slots = np.ascontiguousarray(request_slot, dtype=np.int32)
@@ -374,23 +403,27 @@ def lora_sgmv_shrink(dims: LoraDims, family: int, x, A_stack, routing: LoraRouti
 
 
 def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, routing: LoraRouting, y,
-                     path: int = PATH_AUTO, stream=None) -> None:
-    """y[:end] += per-segment B[slot] . u, in place, asynchronously on the stream."""
+                     path: int = PATH_AUTO, stream=None, bias=None) -> None:
+    """y[:end] += per-segment B[slot] . u (+ bias[slot] when a bias stack
+    [L, out] is given), in place, asynchronously on the stream."""
     dc, rc = dims.c(), routing.c()
     _check(_load().lora_sgmv_expand(ctypes.byref(dc), family, _dev_ptr(u, "u"),
-                                     _dev_ptr(B_stack, "B_stack"), ctypes.byref(rc), _dev_ptr(y, "y"),
-                                     _row_stride(y, "y"), int(path), _stream_handle(stream)),
+                                     _dev_ptr(B_stack, "B_stack"), _dev_ptr(bias, "bias"), ctypes.byref(rc),
+                                     _dev_ptr(y, "y"), _row_stride(y, "y"), int(path),
+                                     _stream_handle(stream)),
            "lora_sgmv_expand")
 
 
 def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, routing: LoraRouting, y,
-                    workspace, path: int = PATH_AUTO, stream=None) -> None:
-    """y[:end] += per-segment B[slot] . (A[slot] . x), shrink and expand in one call."""
+                    workspace, path: int = PATH_AUTO, stream=None, bias=None) -> None:
+    """y[:end] += per-segment B[slot] . (A[slot] . x) (+ bias[slot] when a
+    bias stack [L, out] is given), shrink and expand in one call."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dc, rc = dims.c(), routing.c()
     _check(_load().lora_sgmv_delta(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
                                     _dev_ptr(A_stack, "A_stack"), _dev_ptr(B_stack, "B_stack"),
-                                    ctypes.byref(rc), _dev_ptr(y, "y"), _row_stride(y, "y"),
+                                    _dev_ptr(bias, "bias"), ctypes.byref(rc), _dev_ptr(y, "y"),
+                                    _row_stride(y, "y"),
                                     _dev_ptr(workspace, "workspace"), ws_bytes, int(path),
                                     _stream_handle(stream)),
            "lora_sgmv_delta")

@@ -335,6 +335,34 @@ lora_status_t lora_pack_family(const lora_dims_t* dims, int32_t family, int32_t 
     return LORA_OK;
 }
 
+lora_status_t lora_pack_bias(const lora_dims_t* dims, int32_t family, uint32_t slice_mask,
+                             const float* const* bias_slices, void* bias_out)
+{
+    FamilyShape fs;
+    lora_status_t st = family_shape(dims, family, &fs);
+    if (st != LORA_OK)
+        return st;
+    if (!bias_out)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (slice_mask >> fs.n_s)
+        return LORA_ERR_INVALID_ADAPTER;
+    for (int s = 0; s < fs.n_s; ++s)
+        if (((slice_mask >> s) & 1u) && (!bias_slices || !bias_slices[s]))
+            return LORA_ERR_INVALID_ARGUMENT;
+    for (int s = 0; s < fs.n_s; ++s) {
+        const bool on = (slice_mask >> s) & 1u;
+        for (int64_t o = 0; o < fs.widths[s]; ++o) {
+            const float v = on ? bias_slices[s][o] : 0.0f;
+            const int64_t at = fs.offs[s] + o;
+            if (fs.elem == 2)
+                ((uint16_t*)bias_out)[at] = to_bf16(v);
+            else
+                ((float*)bias_out)[at] = v;
+        }
+    }
+    return LORA_OK;
+}
+
 lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
                                  const int64_t* row_offsets, int32_t max_num_loras,
                                  int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,

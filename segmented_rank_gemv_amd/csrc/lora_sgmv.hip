@@ -608,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void zero_words(uint4* p, int64_t n)
 // expand
 
 struct ExpandArgs {
+    const void* bias;  // [L][out_f] per-adapter bias added in the epilogue, or null
     const float* u;  // slab s at u + s * slab, each [end][C]
     int64_t slab;
     int S;
@@ -727,10 +728,49 @@ __device__ __forceinline__ int b_swizzle(int f)
         return (f & 1) | (((f >> 1) & 1) << 1) | (((f >> 3) & 1) << 2);
 }
 
+// The adapter's bias for the 8 features a lane holds in the MFMA layout
+// (acc0: f .. f+3, acc1: f+4 .. f+7), added to the accumulators ([MAX-lora]
+// LoRAType BIAS: a bias attached to B).  b holds the 8 bf16 values.
+__device__ __forceinline__ void add_bias8(uint4 b, f32x4_t& acc0, f32x4_t& acc1)
+{
+    acc0[0] += bf2f(b.x & 0xFFFFu);
+    acc0[1] += bf2f(b.x >> 16);
+    acc0[2] += bf2f(b.y & 0xFFFFu);
+    acc0[3] += bf2f(b.y >> 16);
+    acc1[0] += bf2f(b.z & 0xFFFFu);
+    acc1[1] += bf2f(b.z >> 16);
+    acc1[2] += bf2f(b.w & 0xFFFFu);
+    acc1[3] += bf2f(b.w >> 16);
+}
+
+// The MFMA expands stage the tile's bias row (ft bf16 values) in LDS: the
+// first ft / 8 threads load one 16-byte piece each together with the y and B
+// loads (without a bias the size is zero and the load reads zero), store it
+// with the other LDS tiles, and the epilogue reads a lane's 8 values there.
+__device__ __forceinline__ uint4 load_bias_piece(const ExpandArgs& a, const TileInfo& ti, int f0)
+{
+    const Buf bb(reinterpret_cast<const uint16_t*>(a.bias) + (size_t)ti.slot * a.out_f + f0,
+                 a.bias ? (uint32_t)(a.ft * 2) : 0u);
+    return bb.ld16((int)threadIdx.x < (a.ft >> 3) ? (uint32_t)threadIdx.x * 16 : kOOB);
+}
+
+__device__ __forceinline__ void store_bias_piece(const ExpandArgs& a, uint16_t* bls, uint4 v)
+{
+    if (a.bias && (int)threadIdx.x < (a.ft >> 3))
+        *reinterpret_cast<uint4*>(bls + 8 * threadIdx.x) = v;
+}
+
+__device__ __forceinline__ void add_bias8_lds(const ExpandArgs& a, const uint16_t* bls, int f, f32x4_t& acc0,
+                                              f32x4_t& acc1)
+{
+    if (a.bias)
+        add_bias8(*reinterpret_cast<const uint4*>(bls + f), acc0, acc1);
+}
+
 template <int NH>
 __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
                                             const Buf& yb, int ucol0, float* us, float4* part,
-                                            uint16_t* ylds, uint16_t* blds)
+                                            uint16_t* ylds, uint16_t* blds, uint16_t* bls)
 {
     static_assert(NH == 1 || NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
     constexpr int R = 16 * NH;
@@ -760,6 +800,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
         const int p = tid + kThreads * i;
         braw[i] = bb.ld16(p < a.ft * NCH ? (uint32_t)p * 16 : kOOB);
     }
+    const uint4 bpiece = load_bias_piece(a, ti, f0);
     // u next: its loads go out before the wait on y and B
     stage_u(a, ti, ucol0, us, part);
 #pragma unroll
@@ -769,6 +810,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
             *reinterpret_cast<uint4*>(ylds + row * kYLd + 8 * pc) = yraw[i];
         }
     }
+    store_bias_piece(a, bls, bpiece);
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
         const int p = tid + kThreads * i, f = p / NCH, c = p % NCH;
@@ -803,6 +845,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
                 const uint4 yv = *cell;
                 f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
                 f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+                add_bias8_lds(a, bls, 32 * p + 8 * q, acc0, acc1);
 #pragma unroll
                 for (int kh = 0; kh < NH; ++kh) {
                     const int c = 2 * kh + (q & 1);
@@ -849,7 +892,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
 template <int NH>
 __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileInfo& ti, int f0,
                                                const Buf& yb, int ucol0, float* us, float4* part,
-                                               uint16_t* blds)
+                                               uint16_t* blds, uint16_t* bls)
 {
     static_assert(NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
     constexpr int R = 16 * NH;
@@ -876,7 +919,9 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
         const int p = tid + kThreads * i;
         braw[i] = bb.ld16(p < a.ft * NCH ? (uint32_t)p * 16 : kOOB);
     }
+    const uint4 bpiece = load_bias_piece(a, ti, f0);
     stage_u(a, ti, ucol0, us, part);
+    store_bias_piece(a, bls, bpiece);
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
         const int p = tid + kThreads * i, f = p / NCH, c = p % NCH;
@@ -910,6 +955,7 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
             const uint4 yv = yraw[p];
             f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
             f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+            add_bias8_lds(a, bls, 32 * p + 8 * q, acc0, acc1);
 #pragma unroll
             for (int kh = 0; kh < NH; ++kh) {
                 const int c = 2 * kh + (q & 1);
@@ -947,7 +993,7 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
 // y and (for NH <= 2) B fragments are loaded before u is staged.
 template <int NH>
 __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileInfo& ti, int f0,
-                                            const Buf& yb, int ucol0, float* us, float4* part)
+                                            const Buf& yb, int ucol0, float* us, float4* part, uint16_t* bls)
 {
     constexpr int kMaxPairs = kExpandCols / 32;
     constexpr bool kPrefetchB = NH == 1;
@@ -974,8 +1020,10 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
                     bfr[p][h][kh] = ld16(Bb + (size_t)(min(p, np - 1) * 32 + mrow + 4 * h) * a.R + 16 * kh +
                                          8 * (q & 1));
     }
+    const uint4 bpiece = load_bias_piece(a, ti, f0);
 
     stage_u(a, ti, ucol0, us, part);
+    store_bias_piece(a, bls, bpiece);
     __syncthreads();
     if (16 * w >= ti.n)
         return;
@@ -1003,6 +1051,7 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
             const uint4 yv = yraw[p];
             f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
             f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+            add_bias8_lds(a, bls, 32 * p + 8 * q, acc0, acc1);
 #pragma unroll
             for (int kh = 0; kh < NH; ++kh) {
                 uint4 b0, b1;
@@ -1095,11 +1144,13 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo&
         for (int i = 0; i < 2; ++i) {
             const int row = rr + (p0 + i) * rp;
             if (row < ti.n) {
-                float out[8];
+                float out[8], bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 Vec8<T>::unpack(yraw[i], out);
+                if (a.bias)
+                    Vec8<T>::load(reinterpret_cast<const T*>(a.bias) + (size_t)ti.slot * a.out_f + f, bias);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    out[e] += delta[i][e];
+                    out[e] += bias[e] + delta[i][e];
                 Vec8<T>::store_buf(yb, (uint32_t)(row * a.ldy + f) * E, out);
             }
         }
@@ -1120,6 +1171,8 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     // ranks 32 and 64: B tile alone, at ylds
     uint16_t* ylds = reinterpret_cast<uint16_t*>(part + kThreads);
     uint16_t* blds = ylds + kTileM * kYLd;
+    // the bias row of the tile, after the y and B tiles (only with a bias)
+    uint16_t* bls = ylds + (NH == 1 ? kTileM * kYLd + kExpandCols * 16 : NH == 2 || NH == 4 ? kExpandCols * 16 * NH : 0);
 
     const int lin = blockIdx.x;
     const int ftile = lin % a.n_ftiles;
@@ -1135,19 +1188,19 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     // to two or one); rank 48 reads both from memory
     if constexpr (NH > 0 && MODE == kMfmaOnly) {
         if constexpr (NH == 1)
-            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
+            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds, bls);
         else if constexpr (NH == 2 || NH == 4)
-            expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
+            expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds, bls);
         else
-            expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
+            expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part, bls);
     } else if constexpr (NH > 0 && MODE == kMixed) {
         if (ti.glen > a.valu_max) {
             if constexpr (NH == 1)
-                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds);
+                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds, bls);
             else if constexpr (NH == 2 || NH == 4)
-                expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds);
+                expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds, bls);
             else
-                expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part);
+                expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part, bls);
         } else
             expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
     } else {
@@ -1189,6 +1242,7 @@ constexpr int kFusedHostFt = 64;
 // The fields every workgroup needs before its first data load come first,
 // so that they are one contiguous run of the argument segment.
 struct FusedArgs {
+    const uint16_t* bias;  // [L][out_f] per-adapter bias added in the epilogue, or null
     const uint16_t* x;
     int64_t ldx;
     const uint16_t* A;  // [L][a_slot] in the tiled A layout (a_tiled_index)
@@ -1282,6 +1336,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const Buf yb(a.y + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * 2));
     const uint32_t yoff = (pair && tok) ? (uint32_t)(l16 * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
     const uint4 yraw = yb.ld16(yoff);
+    // the wave's 8 bias values, read with y (zero without a bias)
+    const Buf biasb(a.bias + (size_t)ti.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
+    const uint4 braw_bias = biasb.ld16(pair ? (uint32_t)(32 * w + 8 * q) * 2 : kOOB);
     // B rows as the M operand, permuted: row i of block h is feature
     // 32 w + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
     const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
@@ -1409,6 +1466,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     }
     f32x4_t acc0 = {bf2f(yraw.x & 0xFFFFu), bf2f(yraw.x >> 16), bf2f(yraw.y & 0xFFFFu), bf2f(yraw.y >> 16)};
     f32x4_t acc1 = {bf2f(yraw.z & 0xFFFFu), bf2f(yraw.z >> 16), bf2f(yraw.w & 0xFFFFu), bf2f(yraw.w >> 16)};
+    if (a.bias)
+        add_bias8(braw_bias, acc0, acc1);
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) {
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[0][kh]), uf[kh], acc0, 0,
@@ -1591,9 +1650,10 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
 bool nh_possible(const Common& c, const ExpandArgs& a) { return expand_mfma_ok(c) && a.valu_max < kTileM; }
 
 lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, const void* B_stack,
-                         void* y, int64_t ldy, int32_t path, hipStream_t s)
+                         const void* bias, void* y, int64_t ldy, int32_t path, hipStream_t s)
 {
     ExpandArgs a;
+    a.bias = bias;
     a.u = u;
     a.slab = slab;
     a.S = S;
@@ -1623,7 +1683,8 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     const size_t lds = (size_t)kTileM * c.fs.R * sizeof(float) + kThreads * sizeof(float4) +
                        (nh == 1   ? ((size_t)kTileM * kYLd + (size_t)kExpandCols * c.fs.R) * sizeof(uint16_t)
                         : nh == 2 || nh == 4 ? (size_t)kExpandCols * c.fs.R * sizeof(uint16_t)
-                                             : 0);
+                                             : 0) +
+                       (nh && bias ? (size_t)kExpandCols * sizeof(uint16_t) : 0);
     const dim3 g((unsigned)grid), b(kThreads);
     const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
 #define LORA_EXPAND_NH(NHV)                                                                       \
@@ -1673,9 +1734,10 @@ bool fused_auto(const Common& c)
 }
 
 lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void* A_stack, const void* B_stack,
-                        void* y, int64_t ldy, hipStream_t s)
+                        const void* bias, void* y, int64_t ldy, hipStream_t s)
 {
     FusedArgs a;
+    a.bias = reinterpret_cast<const uint16_t*>(bias);
     a.x = reinterpret_cast<const uint16_t*>(x);
     a.ldx = ldx;
     a.A = reinterpret_cast<const uint16_t*>(A_stack);
@@ -1840,8 +1902,8 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
 }
 
 lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const float* u,
-                               const void* B_stack, const lora_routing_t* routing, void* y,
-                               int64_t ldy, int32_t path, void* stream)
+                               const void* B_stack, const void* bias_stack, const lora_routing_t* routing,
+                               void* y, int64_t ldy, int32_t path, void* stream)
 {
     Common c;
     lora_status_t st = check_common(dims, family, path, routing, &c);
@@ -1852,15 +1914,15 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
     if (!u || !B_stack || !y || !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(u) ||
-        !aligned16(B_stack) || !aligned16(y))
+        !aligned16(B_stack) || !aligned16(y) || !aligned16(bias_stack))
         return LORA_ERR_INVALID_ARGUMENT;
-    return run_expand(c, u, 0, 1, B_stack, y, ldy, path, reinterpret_cast<hipStream_t>(stream));
+    return run_expand(c, u, 0, 1, B_stack, bias_stack, y, ldy, path, reinterpret_cast<hipStream_t>(stream));
 }
 
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
-                              const void* A_stack, const void* B_stack, const lora_routing_t* routing,
-                              void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
-                              int32_t path, void* stream)
+                              const void* A_stack, const void* B_stack, const void* bias_stack,
+                              const lora_routing_t* routing, void* y, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, int32_t path, void* stream)
 {
     Common c;
     lora_status_t st = check_common(dims, family, path, routing, &c);
@@ -1873,14 +1935,14 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
         return LORA_OK;
     if (!x || !A_stack || !B_stack || !y || !workspace || !row_ok(ldx, c.fs.in_f, c.fs.elem) ||
         !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(x) || !aligned16(y) || !aligned16(A_stack) ||
-        !aligned16(B_stack) || !aligned16(workspace))
+        !aligned16(B_stack) || !aligned16(workspace) || !aligned16(bias_stack))
         return LORA_ERR_INVALID_ARGUMENT;
     const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
     if (workspace_bytes < delta_workspace(plan))
         return LORA_ERR_CAPACITY;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c)))
-        return run_fused(c, x, ldx, A_stack, B_stack, y, ldy, s);
+        return run_fused(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
     float* slabs = reinterpret_cast<float*>(workspace);
     st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
     if (st != LORA_OK)
@@ -1896,7 +1958,7 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
             return LORA_ERR_DEVICE;
         S = 1;
     }
-    return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, y, ldy, path, s);
+    return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, bias_stack, y, ldy, path, s);
 }
 
 // Bytes of one slot of each stack: A_qkv, B_qkv, A_o, B_o.

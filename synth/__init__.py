@@ -6,7 +6,7 @@ It only *draws* raw inputs:
 * request lengths and per-request slot ids (-1 = base model),
 * per-slot adapter ranks,
 * unscaled per-projection adapter matrices in the PEFT layout
-  (``lora_A`` [r, in], ``lora_B`` [out, r], fp32),
+  (``lora_A`` [r, in], ``lora_B`` [out, r], fp32) and LoRA biases [out],
 * activations ``x`` and base-layer outputs ``y``.
 
 It performs none of the method's arithmetic: no scaling, padding, QKV fusion,
@@ -23,6 +23,7 @@ from .workloads import (  # noqa: F401
     bf16_bits,
     draw_activations,
     draw_adapter,
+    draw_bias,
     draw_mlp_activations,
     draw_mlp_adapter,
     draw_ranks,

@@ -19,7 +19,7 @@ PROJECTIONS = ("q", "k", "v", "o")
 MLP_PROJECTIONS = ("gate", "up", "down")
 
 # stream ids of the counter-addressed generators
-_S_REQ, _S_RANK, _S_ADAPTER, _S_ACT, _S_MLP_ADAPTER, _S_MLP_ACT = 1, 2, 3, 4, 5, 6
+_S_REQ, _S_RANK, _S_ADAPTER, _S_ACT, _S_MLP_ADAPTER, _S_MLP_ACT, _S_BIAS = 1, 2, 3, 4, 5, 6, 7
 
 B_VARIANCE = 0.02
 
@@ -177,6 +177,18 @@ def draw_adapter(w: Workload, layer: int, slot: int, rank: int) -> Dict[str, Tup
         a = rng.standard_normal((rank, fin), dtype=np.float32) * np.float32(1.0 / np.sqrt(fin))
         b = rng.standard_normal((fout, rank), dtype=np.float32) * np.float32(np.sqrt(B_VARIANCE))
         out[p] = (a.astype(np.float32), b.astype(np.float32))
+    return out
+
+
+def draw_bias(w: Workload, layer: int, slot: int, projections=PROJECTIONS) -> Dict[str, np.ndarray]:
+    """Unscaled fp32 LoRA biases of one adapter in one layer: {p: bias [out_p]}.
+    Their spread (4 sqrt(B_VARIANCE)) is of the order of a rank-16 delta."""
+    rng = _rng(w, _S_BIAS, layer, slot)
+    out = {}
+    for p in projections:
+        _, fout = w.proj_shape(p)
+        out[p] = (rng.standard_normal(fout, dtype=np.float32) * np.float32(4.0 * np.sqrt(B_VARIANCE))
+                  ).astype(np.float32)
     return out
 
 

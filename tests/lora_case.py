@@ -65,6 +65,25 @@ def pack_stacks(w: synth.Workload, layer: int, ranks: np.ndarray, targets="qkvo"
     return stacks
 
 
+def pack_bias_stacks(w: synth.Workload, layer: int, targets="qkvo") -> Dict[str, np.ndarray]:
+    """Bias stacks [L, out] of one layer: bias_qkv / bias_o packed by the
+    product library and, under "ref", by the oracle."""
+    d = dims_of(w)
+    fams = (("bias_qkv", srg.FAMILY_QKV, "qkv"), ("bias_o", srg.FAMILY_O, "o"))
+    out = {k: [] for k, _, _ in fams}
+    ref = {k: [] for k, _, _ in fams}
+    for s in range(w.max_num_loras):
+        b = synth.draw_bias(w, layer, s)
+        for key, fam, projs in fams:
+            sl = [b[p] if p in targets else None for p in projs]
+            out[key].append(srg.lora_pack_bias(d, fam, sl))
+            widths = srg.lora_family_shape(d, fam)[2]
+            ref[key].append(oracle.pack_bias(widths, w.dtype, sl))
+    stacks = {k: np.stack(v) for k, v in out.items()}
+    stacks["ref"] = {k: np.stack(v) for k, v in ref.items()}
+    return stacks
+
+
 def to_dev(a: np.ndarray, dtype: str):
     import torch
     if dtype == "bf16":
@@ -90,7 +109,7 @@ class GpuLayer:
 
     def __init__(self, w: synth.Workload, stacks: Dict[str, np.ndarray], lengths: np.ndarray,
                  slots: np.ndarray, acts: Dict[str, np.ndarray], pad_rows: int = 0,
-                 pad_cols: int = 0):
+                 pad_cols: int = 0, bias: Optional[Dict[str, np.ndarray]] = None):
         import torch
         self.w = w
         self.dims = dims_of(w)
@@ -105,6 +124,7 @@ class GpuLayer:
         self.end = self.rt["end"]
         self.G = self.rt["num_groups"]
         self.st = {k: to_dev(v, w.dtype) for k, v in stacks.items() if k != "ref"}
+        self.bias = None if bias is None else {k: to_dev(v, w.dtype) for k, v in bias.items() if k != "ref"}
         # routing with host copies (kernel-argument routing) and device-only
         self.routing = {"host": srg.LoraRouting.from_host(self.rt, host_copy=True),
                         "device": srg.LoraRouting.from_host(self.rt, host_copy=False)}
@@ -141,13 +161,17 @@ class GpuLayer:
             xk, yk = ("x_qkv", "y_qkv") if fam == srg.FAMILY_QKV else ("x_o", "y_o")
             A = self.st["A_qkv" if fam == srg.FAMILY_QKV else "A_o"]
             B = self.st["B_qkv" if fam == srg.FAMILY_QKV else "B_o"]
+            bias = None if self.bias is None else self.bias["bias_qkv" if fam == srg.FAMILY_QKV else "bias_o"]
             if fused:
-                log(f"  launch delta family={fam} path={path} routing={routing} end={self.end} G={self.G}")
-                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path)
+                log(f"  launch delta family={fam} path={path} routing={routing} end={self.end} G={self.G}"
+                    f" bias={bias is not None}")
+                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path,
+                                    bias=bias)
                 continue
-            log(f"  launch shrink+expand family={fam} path={path} routing={routing} end={self.end} G={self.G}")
+            log(f"  launch shrink+expand family={fam} path={path} routing={routing} end={self.end} G={self.G}"
+                f" bias={bias is not None}")
             srg.lora_sgmv_shrink(self.dims, fam, self.dev[xk], A, rt, self.u[fam], self.ws[fam], path)
-            srg.lora_sgmv_expand(self.dims, fam, self.u[fam], B, rt, self.dev[yk], path)
+            srg.lora_sgmv_expand(self.dims, fam, self.u[fam], B, rt, self.dev[yk], path, bias=bias)
         import torch
         torch.cuda.synchronize()
 
@@ -165,17 +189,20 @@ class GpuLayer:
 
 
 def oracle_layer(w: synth.Workload, stacks: Dict[str, np.ndarray], lengths, slots, acts,
-                 requests: Optional[Sequence[int]] = None, token_rows=None):
+                 requests: Optional[Sequence[int]] = None, token_rows=None,
+                 bias: Optional[Dict[str, np.ndarray]] = None):
     """Oracle reference of both families: {family: {request: (rows, y_ref, u)}}."""
     offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     R = w.max_lora_rank
     st = stacks["ref"]
+    bq = None if bias is None else bias["ref"]["bias_qkv"]
+    bo = None if bias is None else bias["ref"]["bias_o"]
     ref = {}
     ref[srg.FAMILY_QKV] = oracle.reference_family(acts["x_qkv"], acts["y_qkv"], offs, slots,
                                                   st["A_qkv"], st["B_qkv"],
-                                                  [w.nq, w.nkv, w.nkv], R, w.dtype, requests, token_rows)
+                                                  [w.nq, w.nkv, w.nkv], R, w.dtype, requests, token_rows, bq)
     ref[srg.FAMILY_O] = oracle.reference_family(acts["x_o"], acts["y_o"], offs, slots, st["A_o"],
-                                                st["B_o"], [w.hidden], R, w.dtype, requests, token_rows)
+                                                st["B_o"], [w.hidden], R, w.dtype, requests, token_rows, bo)
     return ref
 
 

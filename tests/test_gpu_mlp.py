@@ -21,13 +21,13 @@ def mdims(w):
                         w.dtype, w.intermediate)
 
 
-def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0):
+def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0, with_bias=False):
     import torch
     d = mdims(w)
     in_f, n_s, widths, out_f = srg.lora_family_shape(d, fam)
     names = ("gate", "up") if fam == srg.FAMILY_GATE_UP else ("down",)
     xk, yk = ("x_gu", "y_gu") if fam == srg.FAMILY_GATE_UP else ("x_down", "y_down")
-    A, B, Ar, Br = [], [], [], []
+    A, B, Ar, Br, bl, br = [], [], [], [], [], []
     for s in range(w.max_num_loras):
         weights = synth.draw_mlp_adapter(w, layer, s, int(ranks[s]))
         sl = [weights[p] for p in names]
@@ -35,6 +35,11 @@ def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0):
         orc = oracle.pack_family(in_f, widths, w.max_lora_rank, w.dtype, int(ranks[s]), w.lora_alpha,
                                  w.use_rslora, True, sl)
         A.append(lib["A"]), B.append(lib["B"]), Ar.append(orc["A"]), Br.append(orc["B"])
+        if with_bias:
+            bias = synth.draw_bias(w, layer, s, names)
+            bsl = [bias[p] for p in names]
+            bl.append(srg.lora_pack_bias(d, fam, bsl))
+            br.append(oracle.pack_bias(widths, w.dtype, bsl))
     lengths = np.asarray(lengths, np.int64)
     slots = np.asarray(slots, np.int32)
     offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
@@ -50,19 +55,20 @@ def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0):
                     dtype=torch.int32, device="cuda")
     routing = srg.LoraRouting.from_host(rt)
     As, Bs = to_dev(np.stack(A), w.dtype), to_dev(np.stack(B), w.dtype)
-    log(f"  mlp family={fam} path={path} fused={fused} T={T} end={end} G={rt['num_groups']}")
+    bs = to_dev(np.stack(bl), w.dtype) if with_bias else None
+    log(f"  mlp family={fam} path={path} fused={fused} T={T} end={end} G={rt['num_groups']} bias={with_bias}")
     if fused:
-        srg.lora_sgmv_delta(d, fam, x, As, Bs, routing, y, ws, PATHS[path])
+        srg.lora_sgmv_delta(d, fam, x, As, Bs, routing, y, ws, PATHS[path], bias=bs)
     else:
         u = torch.zeros((max(end, 1), n_s * w.max_lora_rank), dtype=torch.float32, device="cuda")
         srg.lora_sgmv_shrink(d, fam, x, As, routing, u, ws, PATHS[path])
-        srg.lora_sgmv_expand(d, fam, u, Bs, routing, y, PATHS[path])
+        srg.lora_sgmv_expand(d, fam, u, Bs, routing, y, PATHS[path], bias=bs)
     torch.cuda.synchronize()
     ys = from_dev(y)
     got = np.empty_like(ys[:T])
     got[order] = ys[:T]
     ref = oracle.reference_family(acts[xk], acts[yk], offs, slots, np.stack(Ar), np.stack(Br), list(widths),
-                                  w.max_lora_rank, w.dtype)
+                                  w.max_lora_rank, w.dtype, bias_stack=np.stack(br) if with_bias else None)
     g_all, r_all = [], []
     for i, (rows, yref, uref) in ref.items():
         g = got[int(offs[i]) + rows]
@@ -94,4 +100,26 @@ def test_small_mlp_ragged_every_path(fam, path):
     slots = [0, 1, 2, 3, 0, 1, -1, 2, 3][:len(lengths)]
     ey = run_family(w, fam, lengths, slots, np.array([16, 8, 4, 12], np.int32), path, path == "fused")
     log(f"[mlp-small] family={fam} path={path} y_rel={ey:.3e}")
+    assert ey <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("path", ["auto", "valu", "mfma"])
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("fam", [srg.FAMILY_GATE_UP, srg.FAMILY_DOWN])
+def test_mlp_with_lora_bias(fam, fused, path):
+    """The MLP families with a LoRA bias per slot: the Llama-3-8B MLP decode
+    batch (auto) and the small ragged case (VALU, MFMA)."""
+    if path == "auto":
+        w = synth.get_workload("mlp")
+        lengths, slots = synth.draw_requests(w)
+        ranks = synth.draw_ranks(w)
+    else:
+        base = synth.get_workload("mlp")
+        w = synth.Workload(**{**base.__dict__, "hidden": 256, "n_heads": 4, "n_kv_heads": 2, "head_dim": 64,
+                              "intermediate": 704, "max_num_loras": 4})
+        lengths = [1, 15, 16, 33, 64, 65, 3, 0, 20]
+        slots = [0, 1, 2, 3, 0, 1, -1, 2, 3]
+        ranks = np.array([16, 8, 4, 12], np.int32)
+    ey = run_family(w, fam, lengths, slots, ranks, path, fused, with_bias=True)
+    log(f"[mlp-bias] family={fam} fused={fused} path={path} y_rel={ey:.3e}")
     assert ey <= TOL["bf16"]
