@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 6
+#define LORA_ABI_VERSION 7
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -165,29 +165,6 @@ lora_status_t lora_pack_adapter(const lora_dims_t* dims, int32_t rank, float lor
                                 const float* A_o, const float* B_o, void* A_qkv_out,
                                 void* B_qkv_out, void* A_o_out, void* B_o_out);
 
-/* ---------------------------------------------------------------------------
- * lora_build_routing — host, synchronous.
- *
- * [MAX-V3] sort_lora_batch(): requests of one adapter adjacent, ordered by
- * slot id, base requests (slot -1) last; order within a slot is arrival order
- * (stable).  [MAX-V3] get_lora_graph_inputs(): consecutive same-slot requests
- * form a group; grouping stops at the first base request; `end` is the
- * number of LoRA-routed tokens.  Requests with zero tokens keep their place
- * (a group may be empty).
- *
- * Inputs:  request_slot[num_requests] in [-1, max_num_loras);
- *          row_offsets[num_requests+1], row_offsets[0] == 0, non-decreasing,
- *          request i owns tokens [row_offsets[i], row_offsets[i+1]).
- * Outputs: perm[num_requests] (sorted position -> arrival index),
- *          sorted_row_offsets[num_requests+1],
- *          lora_ids[G] (capacity max_num_loras), grouped_offsets[G+1]
- *          (capacity max_num_loras+1; [0] = 0, [G] = end; token offsets in the
- *          sorted batch), *num_groups = G, *end.
- * Errors:  LORA_ERR_SLOT_OUT_OF_RANGE for a bad slot; LORA_ERR_INVALID_ARGUMENT
- *          for bad offsets, null pointers or end >= 2^31.
- * A base-only or empty batch gives G = 0, end = 0; the device calls then do
- * nothing.
- */
 /* Host, synchronous: pack one adapter's projections of one family into one
  * slot's A and B — the steps of lora_pack_adapter (validate, scale B by
  * alpha/r or alpha/sqrt(r), zero-pad to max_lora_rank, concatenate the
@@ -216,10 +193,57 @@ lora_status_t lora_pack_family(const lora_dims_t* dims, int32_t family, int32_t 
 lora_status_t lora_pack_bias(const lora_dims_t* dims, int32_t family, uint32_t slice_mask,
                              const float* const* bias_slices, void* bias_out);
 
+/* ---------------------------------------------------------------------------
+ * lora_build_routing — host, synchronous.
+ *
+ * [MAX-V3] sort_lora_batch(): requests of one adapter adjacent, ordered by
+ * slot id, base requests (slot -1) last; order within a slot is arrival order
+ * (stable).  [MAX-V3] get_lora_graph_inputs(): consecutive same-slot requests
+ * form a group; grouping stops at the first base request; `end` is the
+ * number of LoRA-routed tokens.  Requests with zero tokens keep their place
+ * (a group may be empty).
+ *
+ * Inputs:  request_slot[num_requests] in [-1, max_num_loras);
+ *          row_offsets[num_requests+1], row_offsets[0] == 0, non-decreasing,
+ *          request i owns tokens [row_offsets[i], row_offsets[i+1]).
+ * Outputs: perm[num_requests] (sorted position -> arrival index),
+ *          sorted_row_offsets[num_requests+1],
+ *          lora_ids[G] (capacity max_num_loras), grouped_offsets[G+1]
+ *          (capacity max_num_loras+1; [0] = 0, [G] = end; token offsets in the
+ *          sorted batch), *num_groups = G, *end.
+ * Errors:  LORA_ERR_SLOT_OUT_OF_RANGE for a bad slot; LORA_ERR_INVALID_ARGUMENT
+ *          for bad offsets, null pointers or end >= 2^31.
+ * A base-only or empty batch gives G = 0, end = 0; the device calls then do
+ * nothing.
+ */
 lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_slot,
                                  const int64_t* row_offsets, int32_t max_num_loras,
                                  int32_t* perm, int64_t* sorted_row_offsets, int32_t* lora_ids,
                                  int32_t* grouped_offsets, int32_t* num_groups, int64_t* end);
+
+/* ---------------------------------------------------------------------------
+ * lora_build_token_routing — host, synchronous.
+ *
+ * Per-token routing ([vLLM] §6 多 LoRA 并发路由机制): token_lora_mapping
+ * gives every token of the batch its GPU slot (-1: no adapter), in the
+ * caller's token order, and the batch is not reordered in memory.  Tokens
+ * are ordered by slot, stably, base tokens last (the kernels' view, as
+ * token_indices_sorted_by_lora_ids orders them for locality); consecutive
+ * tokens of one slot form a group.  This is lora_build_routing with one
+ * request per token.
+ *
+ * Inputs:  token_slot[num_tokens] in [-1, max_num_loras).
+ * Outputs: token_indices_sorted[num_tokens] (sorted position -> token row),
+ *          lora_ids[G] (capacity max_num_loras), grouped_offsets[G+1]
+ *          (capacity max_num_loras+1), *num_groups = G, *end = the number
+ *          of tokens with a slot.  Pass token_indices_sorted (its first end
+ *          entries, on the device) as lora_routing_t.token_rows.
+ * Errors:  LORA_ERR_SLOT_OUT_OF_RANGE for a bad slot; LORA_ERR_INVALID_ARGUMENT
+ *          for null pointers or num_tokens outside [0, 2^31).
+ */
+lora_status_t lora_build_token_routing(int32_t num_tokens, const int32_t* token_slot, int32_t max_num_loras,
+                                       int32_t* token_indices_sorted, int32_t* lora_ids,
+                                       int32_t* grouped_offsets, int32_t* num_groups, int64_t* end);
 
 /* Workspace bytes that lora_sgmv_shrink and lora_sgmv_delta need for a
  * family, for any batch with at most max_tokens LoRA-routed tokens.  The
@@ -247,6 +271,18 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
  *                  the device arrays (which may then be NULL) before its first
  *                  data load.  They are read at call time: launches recorded
  *                  into a HIP graph keep the routing of the recording call.
+ * token_rows, num_rows
+ *                  per-token routing (lora_build_token_routing): NULL = the
+ *                  rows of x, u and y are in sorted order (row t is sorted
+ *                  position t).  Otherwise token_rows is a device
+ *                  int32[end]: sorted position t reads row token_rows[t] of
+ *                  x and updates that row of y, where x and y hold num_rows
+ *                  rows in the caller's order; u stays in sorted order.  The
+ *                  entries must be distinct (two positions on one y row
+ *                  race); an entry outside [0, num_rows) reads zeros and
+ *                  writes nothing.  Requires end <= num_rows and
+ *                  (num_rows + 1) * row stride * element size < 2^32 bytes
+ *                  for x and y.  Rows not listed are neither read nor written.
  * A base-only or empty batch (G = 0 or end = 0) makes every device call a
  * no-op (the base-only routing of [MAX-lora] 运行时工作流与调度交互 — all tokens
  * on slot 0 holding all-zero adapters — is also valid and leaves y as is).
@@ -262,6 +298,8 @@ typedef struct lora_routing {
     int64_t end;
     const int32_t* host_lora_ids;
     const int32_t* host_grouped_offsets;
+    const int32_t* token_rows;
+    int64_t num_rows;
 } lora_routing_t;
 
 /* ---------------------------------------------------------------------------

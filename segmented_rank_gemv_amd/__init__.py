@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     library_path,
     lora_abi_version,
     lora_build_routing,
+    lora_build_token_routing,
     lora_family_shape,
     lora_pack_adapter,
     lora_pack_family,

@@ -44,7 +44,8 @@ class _LoraDims(ctypes.Structure):
 class _LoraRouting(ctypes.Structure):
     _fields_ = [("lora_ids", ctypes.c_void_p), ("grouped_offsets", ctypes.c_void_p),
                 ("num_groups", ctypes.c_int32), ("end", ctypes.c_int64),
-                ("host_lora_ids", ctypes.c_void_p), ("host_grouped_offsets", ctypes.c_void_p)]
+                ("host_lora_ids", ctypes.c_void_p), ("host_grouped_offsets", ctypes.c_void_p),
+                ("token_rows", ctypes.c_void_p), ("num_rows", ctypes.c_int64)]
 
 
 MAX_HOST_GROUPS = 64
@@ -54,11 +55,16 @@ class LoraRouting:
     """The routing triple of a batch for the device calls: lora_ids and
     grouped_offsets as int32 GPU tensors, `end` and the group count on the
     host, and (by default) host copies of the two arrays, which the library
-    passes to the kernels as launch arguments."""
+    passes to the kernels as launch arguments.  For per-token routing,
+    token_rows (int32 GPU tensor, sorted position -> row of x and y) and
+    num_rows (rows of x and y) are set as well."""
 
     def __init__(self, lora_ids, grouped_offsets, num_groups: int, end: int,
                  host_lora_ids: Optional[np.ndarray] = None,
-                 host_grouped_offsets: Optional[np.ndarray] = None):
+                 host_grouped_offsets: Optional[np.ndarray] = None,
+                 token_rows=None, num_rows: int = 0):
+        self.token_rows = token_rows
+        self.num_rows = int(num_rows)
         self.lora_ids = lora_ids
         self.grouped_offsets = grouped_offsets
         self.num_groups = int(num_groups)
@@ -78,8 +84,13 @@ class LoraRouting:
         if device_arrays:
             d_ids = torch.from_numpy(ids if ids.size else np.zeros(1, np.int32)).to(device)
             d_offs = torch.from_numpy(offs).to(device)
+        rows, n_rows = None, 0
+        if "token_indices_sorted" in routing:
+            idx = np.ascontiguousarray(routing["token_indices_sorted"][:routing["end"]], np.int32)
+            rows = torch.from_numpy(idx if idx.size else np.zeros(1, np.int32)).to(device)
+            n_rows = len(routing["token_indices_sorted"])
         return cls(d_ids, d_offs, routing["num_groups"], routing["end"],
-                   ids if host_copy else None, offs if host_copy else None)
+                   ids if host_copy else None, offs if host_copy else None, rows, n_rows)
 
     def c(self) -> _LoraRouting:
         r = _LoraRouting()
@@ -91,6 +102,8 @@ class LoraRouting:
         r.host_lora_ids = None if self.host_lora_ids is None else self.host_lora_ids.ctypes.data
         r.host_grouped_offsets = (None if self.host_grouped_offsets is None
                                   else self.host_grouped_offsets.ctypes.data)
+        r.token_rows = None if self.token_rows is None else _dev_ptr(self.token_rows, "token_rows")
+        r.num_rows = self.num_rows
         return r
 
 
@@ -144,6 +157,8 @@ def _load():
     lib.lora_pack_family.argtypes = [D, i32, i32, ctypes.c_float, i32, i32, u32, P, P, P, P]
     lib.lora_build_routing.restype = i32
     lib.lora_build_routing.argtypes = [i32, P, P, i32, P, P, P, P, P, P]
+    lib.lora_build_token_routing.restype = i32
+    lib.lora_build_token_routing.argtypes = [i32, P, i32, P, P, P, P, P]
     lib.lora_sgmv_workspace_bytes.restype = i32
     lib.lora_sgmv_workspace_bytes.argtypes = [D, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     RT = ctypes.POINTER(_LoraRouting)
@@ -354,6 +369,25 @@ def lora_build_routing(request_slot: np.ndarray, row_offsets: np.ndarray,
                                       _np_ptr(end)), "lora_build_routing")
     g = int(G[0])
     return {"perm": perm[:n].copy(), "sorted_offsets": srt, "lora_ids": ids[:g].copy(),
+            "grouped_offsets": goffs[:g + 1].copy(), "num_groups": g, "end": int(end[0])}
+
+
+def lora_build_token_routing(token_slot: np.ndarray, max_num_loras: int) -> Dict[str, object]:
+    """Per-token routing: token_slot[t] is token t's slot (-1 = none).
+    Returns token_indices_sorted (sorted position -> token), lora_ids,
+    grouped_offsets, num_groups and end."""
+    slots = np.ascontiguousarray(token_slot, dtype=np.int32).reshape(-1)
+    n = slots.size
+    L = int(max_num_loras)
+    idx = np.zeros(max(n, 1), np.int32)
+    ids = np.zeros(max(L, 1), np.int32)
+    goffs = np.zeros(max(L, 1) + 1, np.int32)
+    G = np.zeros(1, np.int32)
+    end = np.zeros(1, np.int64)
+    _check(_load().lora_build_token_routing(n, _np_ptr(slots), L, _np_ptr(idx), _np_ptr(ids), _np_ptr(goffs),
+                                            _np_ptr(G), _np_ptr(end)), "lora_build_token_routing")
+    g = int(G[0])
+    return {"token_indices_sorted": idx[:n].copy(), "lora_ids": ids[:g].copy(),
             "grouped_offsets": goffs[:g + 1].copy(), "num_groups": g, "end": int(end[0])}
 
 

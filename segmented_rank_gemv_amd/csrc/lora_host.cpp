@@ -428,6 +428,46 @@ lora_status_t lora_build_routing(int32_t num_requests, const int32_t* request_sl
     return LORA_OK;
 }
 
+// One request per token: a counting sort by slot (stable, base last) gives
+// the same order, groups and end as lora_build_routing with unit requests,
+// in O(num_tokens + max_num_loras).
+lora_status_t lora_build_token_routing(int32_t num_tokens, const int32_t* token_slot, int32_t max_num_loras,
+                                       int32_t* token_indices_sorted, int32_t* lora_ids,
+                                       int32_t* grouped_offsets, int32_t* num_groups, int64_t* end)
+{
+    if (num_tokens < 0 || max_num_loras < 1 || !lora_ids || !grouped_offsets || !num_groups || !end)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && (!token_slot || !token_indices_sorted))
+        return LORA_ERR_INVALID_ARGUMENT;
+    const int32_t L = max_num_loras;
+    std::vector<int32_t> count((size_t)L + 1, 0);  // bucket L: base tokens
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        const int32_t s = token_slot[t];
+        if (s < -1 || s >= L)
+            return LORA_ERR_SLOT_OUT_OF_RANGE;
+        ++count[s < 0 ? L : s];
+    }
+    std::vector<int32_t> next((size_t)L + 1);
+    int32_t acc = 0, G = 0;
+    grouped_offsets[0] = 0;
+    for (int32_t s = 0; s <= L; ++s) {
+        next[s] = acc;
+        acc += count[s];
+        if (s < L && count[s] > 0) {
+            lora_ids[G] = s;
+            grouped_offsets[G + 1] = acc;
+            ++G;
+        }
+    }
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        const int32_t s = token_slot[t];
+        token_indices_sorted[next[s < 0 ? L : s]++] = t;
+    }
+    *num_groups = G;
+    *end = (int64_t)num_tokens - count[L];
+    return LORA_OK;
+}
+
 lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
                                         int64_t max_tokens, size_t* bytes)
 {

@@ -221,6 +221,35 @@ struct TileInfo {
     int glen;  // tokens in the whole group (decides the kernel path)
 };
 
+// Rows of one token tile in x or y.  Sorted layout (GATHER false): the
+// tile's tokens are rows t0 .. t0 + n - 1 and the tile's buffer resource
+// spans just those rows, so a row past the tile lies outside it.  Per-token
+// routing ([vLLM] §6 LoRAMapping, token_indices_sorted_by_lora_ids): sorted
+// position t0 + r is row idx[t0 + r] of the caller's buffer of nrows rows;
+// the resource spans the whole buffer, and a row past the tile, or an index
+// outside [0, nrows), maps to row nrows, which lies outside it.
+template <bool GATHER>
+struct RowMap {
+    const int* idx;
+    int t0, n;
+    uint32_t nrows;
+    __device__ __forceinline__ uint32_t operator()(int r) const
+    {
+        if constexpr (GATHER)
+            return r < n ? min((uint32_t)idx[t0 + r], nrows) : nrows;
+        else
+            return (uint32_t)r;
+    }
+    template <typename T>
+    __device__ __forceinline__ Buf buf(const T* base, int64_t ld) const
+    {
+        if constexpr (GATHER)
+            return Buf(base, (uint32_t)((int64_t)nrows * ld * (int64_t)sizeof(T)));
+        else
+            return Buf(base + (size_t)t0 * ld, (uint32_t)((int64_t)n * ld * (int64_t)sizeof(T)));
+    }
+};
+
 // Routing as the kernels see it: the device arrays, or (kr != 0) a copy of
 // them carried in the kernel arguments.
 struct RouteArgs {
@@ -228,6 +257,8 @@ struct RouteArgs {
     const int* offs;
     int G, end, L;
     int kr;
+    const int* rows;  // per-token routing: sorted position -> row of x and y (null: rows in sorted order)
+    uint32_t nrows;   // rows of x and y under per-token routing
     int k_offs[LORA_MAX_HOST_GROUPS + 1];
     int k_ids[LORA_MAX_HOST_GROUPS];
 };
@@ -316,7 +347,7 @@ struct ShrinkArgs {
 constexpr int kValuChunk = 32;            // pieces per chunk
 constexpr int kValuPer = kValuChunk / 4;  // pieces per lane and chunk
 
-template <typename T>
+template <typename T, bool GATHER>
 __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int k1, int c0,
                             int c1, float* dst, int64_t dst_ld, float* res, T* xs)
 {
@@ -332,12 +363,18 @@ __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int
     // [kp * per, (kp + 1) * per) of every chunk
     const int pw0 = k0 >> 3, pw1 = (k1 + 7) >> 3;
     const int per = kValuChunk / kparts;  // pieces of a chunk per wave
-    const T* X = reinterpret_cast<const T*>(a.x) + (size_t)ti.t0 * a.ldx;
+    const RowMap<GATHER> xm{a.r.rows, ti.t0, ti.n, a.r.nrows};
     const T* Ab = reinterpret_cast<const T*>(a.A) + (size_t)ti.slot * a.a_slot +
                   (size_t)((c0 >> 4) + b) * 16 * a.in_f;
-    const Buf xb(X, (uint32_t)(ti.n * a.ldx * E));
+    const Buf xb = xm.buf(reinterpret_cast<const T*>(a.x), a.ldx);
     const Buf ab(Ab, (uint32_t)(16 * a.in_f * E));
+    constexpr int XJ = 8 * kValuChunk / kThreads;
     for (int tb = 0; tb < ti.n; tb += 8) {
+        // the rows of this lane's x pieces, the same for every chunk
+        uint32_t xrow[XJ];
+#pragma unroll
+        for (int j = 0; j < XJ; ++j)
+            xrow[j] = xm(tb + (tid + kThreads * j) / kValuChunk);
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -352,12 +389,12 @@ __device__ void shrink_valu(const ShrinkArgs& a, const TileInfo& ti, int k0, int
                     ab, (active && 4 * j < per && p < pw1) ? (uint32_t)((p * 16 + r) * 8) * E : kOOB);
             }
             // x pieces of eight tokens: xs[token][piece] (rows past the tile are zero)
-            typename Vec8<T>::Raw xr[8 * kValuChunk / kThreads];
+            typename Vec8<T>::Raw xr[XJ];
 #pragma unroll
-            for (int j = 0; j < 8 * kValuChunk / kThreads; ++j) {
+            for (int j = 0; j < XJ; ++j) {
                 const int e = tid + kThreads * j, i = e / kValuChunk, pc = e - i * kValuChunk;
                 xr[j] = Vec8<T>::load_raw(
-                    xb, cb + pc < pw1 ? (uint32_t)((tb + i) * a.ldx + 8 * (cb + pc)) * E : kOOB);
+                    xb, cb + pc < pw1 ? (uint32_t)(xrow[j] * a.ldx + 8 * (cb + pc)) * E : kOOB);
             }
             __syncthreads();  // the previous chunk's readers are done with xs
 #pragma unroll
@@ -425,7 +462,7 @@ struct ShrinkLds {
 // each 32-element step is one v_mfma_f32_16x16x32_bf16 per 16-column block,
 // x rows as the M operand and A rows as the N operand.  The wave writes its
 // 16 x cw block of the result directly.
-template <int NB, int KC>
+template <int NB, int KC, bool GATHER>
 __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int k1, int c0,
                             int c1, float* dst, int64_t dst_ld, uint16_t* lds)
 {
@@ -438,21 +475,26 @@ __device__ void shrink_mfma(const ShrinkArgs& a, const TileInfo& ti, int k0, int
     const int l16 = lane & 15, q = lane >> 4;
     uint16_t* lx = lds;
     uint16_t* la = lds + Lay::kX;
-    const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x) + (size_t)ti.t0 * a.ldx;
+    const RowMap<GATHER> xm{a.r.rows, ti.t0, ti.n, a.r.nrows};
     // the group's A blocks in the tiled layout; blocks past the group read as zero
     const uint16_t* Ab =
         reinterpret_cast<const uint16_t*>(a.A) + (size_t)ti.slot * a.a_slot + (size_t)(c0 >> 4) * 16 * a.in_f;
-    const Buf xb(X, (uint32_t)(ti.n * a.ldx * 2));  // rows past the tile read as zero
+    const Buf xb = xm.buf(reinterpret_cast<const uint16_t*>(a.x), a.ldx);  // rows past the tile read as zero
     const Buf ab(Ab, (uint32_t)(((c1 - c0 + 15) >> 4) * 16 * a.in_f * 2));
     const int nchunks = (k1 - k0 + KC - 1) / KC;
 
     uint4 xs[XR], as[AR];
+    // the rows of this thread's x pieces, the same for every chunk
+    uint32_t xrow[XR];
+#pragma unroll
+    for (int i = 0; i < XR; ++i)
+        xrow[i] = xm((tid + kThreads * i) / PIECES);
     auto gload = [&](int ch) {
         const int kb = k0 + ch * KC;
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
-            const int p = tid + kThreads * i, r = p / PIECES, k = kb + 8 * (p % PIECES);
-            xs[i] = xb.ld16(k < k1 ? (uint32_t)(r * a.ldx + k) * 2 : kOOB);
+            const int p = tid + kThreads * i, k = kb + 8 * (p % PIECES);
+            xs[i] = xb.ld16(k < k1 ? (uint32_t)(xrow[i] * a.ldx + k) * 2 : kOOB);
         }
         // A piece p: row p % 16 of block p / (16 PIECES), K piece (p / 16) % PIECES;
         // 16 consecutive threads read one contiguous 256-byte piece group
@@ -536,10 +578,9 @@ enum { kMixed = 0, kMfmaOnly = 1, kValuOnly = 2 };
 // result is u itself; with S splits each workgroup writes its split's slab
 // and the sum over splits is taken later, in split order, by the expand or
 // by reduce_slabs — there is no cross-workgroup synchronisation.
-template <typename T, int NB, int MODE>
+template <typename T, int NB, int MODE, bool GATHER>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
 {
-    constexpr int CB = NB * 16;
     constexpr int KC = kShrinkKC;
     constexpr bool kHasValu = MODE != kValuOnly ? MODE == kMixed : true;
     constexpr bool kHasMfma = MODE != kValuOnly;
@@ -559,21 +600,20 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
         return;
     const int k0 = s * a.kc, k1 = min(k0 + a.kc, a.in_f);
     const int c0 = z * a.cb, c1 = min(c0 + a.cb, a.C);
-    const int cw = c1 - c0;
     float* dst = a.out + (size_t)s * a.slab + (size_t)ti.t0 * a.C + c0;
 
     if constexpr (MODE == kMfmaOnly) {
-        shrink_mfma<NB, KC>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
+        shrink_mfma<NB, KC, GATHER>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
         return;
     }
     if constexpr (MODE == kMixed) {
         if (ti.glen > a.valu_max) {
-            shrink_mfma<NB, KC>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
+            shrink_mfma<NB, KC, GATHER>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<uint16_t*>(smem));
             return;
         }
     }
     if constexpr (kHasValu)
-        shrink_valu<T>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<float*>(smem),
+        shrink_valu<T, GATHER>(a, ti, k0, k1, c0, c1, dst, a.C, reinterpret_cast<float*>(smem),
                        reinterpret_cast<T*>(smem + kValuRes));
 }
 
@@ -767,10 +807,10 @@ __device__ __forceinline__ void add_bias8_lds(const ExpandArgs& a, const uint16_
         add_bias8(*reinterpret_cast<const uint4*>(bls + f), acc0, acc1);
 }
 
-template <int NH>
+template <int NH, bool GATHER>
 __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo& ti, int f0,
-                                            const Buf& yb, int ucol0, float* us, float4* part,
-                                            uint16_t* ylds, uint16_t* blds, uint16_t* bls)
+                                            const Buf& yb, const RowMap<GATHER>& ym, int ucol0, float* us,
+                                            float4* part, uint16_t* ylds, uint16_t* blds, uint16_t* bls)
 {
     static_assert(NH == 1 || NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
     constexpr int R = 16 * NH;
@@ -787,11 +827,24 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
                  (uint32_t)(a.ft * R * 2));
 
     // coalesced y tile: 64 rows x `pieces` pieces, kMaxPairs rounds of 256 pieces
+    // (per-token routing keeps each piece's buffer row for the store)
+    uint32_t yrow[GATHER ? kMaxPairs : 1];
+    if constexpr (GATHER) {
+#pragma unroll
+        for (int i = 0; i < kMaxPairs; ++i)
+            yrow[i] = ym((tid + kThreads * i) / pieces);
+    }
+    auto yrow_of = [&](int i, int row) -> uint32_t {
+        if constexpr (GATHER)
+            return yrow[i];
+        else
+            return (uint32_t)row;
+    };
     uint4 yraw[kMaxPairs];
 #pragma unroll
     for (int i = 0; i < kMaxPairs; ++i) {
         const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
-        yraw[i] = yb.ld16(i < np ? (uint32_t)(row * a.ldy + f0 + 8 * pc) * 2 : kOOB);
+        yraw[i] = yb.ld16(i < np ? (uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2 : kOOB);
     }
     // coalesced B tile: ft rows x NCH chunks (past the tile: kOOB)
     uint4 braw[BR];
@@ -874,7 +927,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
     for (int i = 0; i < kMaxPairs; ++i) {
         if (i < np) {
             const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
-            yb.st16((uint32_t)(row * a.ldy + f0 + 8 * pc) * 2,
+            yb.st16((uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2,
                     *reinterpret_cast<const uint4*>(ylds + row * kYLd + 8 * pc));
         }
     }
@@ -889,10 +942,10 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
 // steps and the four waves, which breaks down once several workgroups share
 // a CU; an LDS tile of y as well would cut the workgroups per CU to one or
 // two.  Waves with no token in the tile help with the B tile only.
-template <int NH>
+template <int NH, bool GATHER>
 __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileInfo& ti, int f0,
-                                               const Buf& yb, int ucol0, float* us, float4* part,
-                                               uint16_t* blds, uint16_t* bls)
+                                               const Buf& yb, const RowMap<GATHER>& ym, int ucol0, float* us,
+                                               float4* part, uint16_t* blds, uint16_t* bls)
 {
     static_assert(NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
     constexpr int R = 16 * NH;
@@ -909,10 +962,11 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
     const Buf bb(reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * R,
                  (uint32_t)(a.ft * R * 2));
 
+    const uint32_t yt = ym(t);  // the buffer row of this lane's token
     uint4 yraw[kMaxPairs];
 #pragma unroll
     for (int p = 0; p < kMaxPairs; ++p)
-        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
+        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(yt * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
     uint4 braw[BR];
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
@@ -972,7 +1026,7 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
             o.y = f2bf_pair(acc0[2], acc0[3]);
             o.z = f2bf_pair(acc1[0], acc1[1]);
             o.w = f2bf_pair(acc1[2], acc1[3]);
-            yb.st16(tok ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
+            yb.st16(tok ? (uint32_t)(yt * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
         }
     }
 }
@@ -991,9 +1045,10 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
 // accumulators: y is the C operand, read and written as 16-byte runs in the
 // MFMA layout itself, and a wave covers 16 rows x 512 contiguous bytes.
 // y and (for NH <= 2) B fragments are loaded before u is staged.
-template <int NH>
+template <int NH, bool GATHER>
 __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileInfo& ti, int f0,
-                                            const Buf& yb, int ucol0, float* us, float4* part, uint16_t* bls)
+                                            const Buf& yb, const RowMap<GATHER>& ym, int ucol0, float* us,
+                                            float4* part, uint16_t* bls)
 {
     constexpr int kMaxPairs = kExpandCols / 32;
     constexpr bool kPrefetchB = NH == 1;
@@ -1005,10 +1060,11 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0
     const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + ((size_t)ti.slot * a.out_f + f0) * a.R;
 
+    const uint32_t yt = ym(t);  // the buffer row of this lane's token
     uint4 yraw[kMaxPairs];
 #pragma unroll
     for (int p = 0; p < kMaxPairs; ++p)
-        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
+        yraw[p] = yb.ld16((p < np && tok) ? (uint32_t)(yt * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB);
     uint4 bfr[kPrefetchB ? kMaxPairs : 1][2][NH];
     if constexpr (kPrefetchB) {
 #pragma unroll
@@ -1073,7 +1129,7 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
             o.y = f2bf_pair(acc0[2], acc0[3]);
             o.z = f2bf_pair(acc1[0], acc1[1]);
             o.w = f2bf_pair(acc1[2], acc1[3]);
-            yb.st16(tok ? (uint32_t)(t * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
+            yb.st16(tok ? (uint32_t)(yt * a.ldy + f0 + 32 * p + 8 * q) * 2 : kOOB, o);
         }
     }
 }
@@ -1083,9 +1139,10 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
 // every y access is a 16-byte run and a wave covers whole row segments.  Row
 // passes go two at a time; the first two are loaded before u is staged.  B is
 // read 8 ranks at a time and reused for both rows.
-template <typename T>
+template <typename T, bool GATHER>
 __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo& ti, int f0,
-                                            const Buf& yb, int ucol0, float* us, float4* part)
+                                            const Buf& yb, const RowMap<GATHER>& ym, int ucol0, float* us,
+                                            float4* part)
 {
     constexpr int E = sizeof(T);
     const int fgroups = a.ft >> 3;
@@ -1098,7 +1155,7 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo&
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = rr + i * rp;
-        yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(row * a.ldy + f) * E : kOOB);
+        yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(ym(row) * a.ldy + f) * E : kOOB);
     }
     stage_u(a, ti, ucol0, us, part);
     __syncthreads();
@@ -1109,7 +1166,7 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo&
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = rr + (p0 + i) * rp;
-                yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(row * a.ldy + f) * E : kOOB);
+                yraw[i] = Vec8<T>::load_raw(yb, row < ti.n ? (uint32_t)(ym(row) * a.ldy + f) * E : kOOB);
             }
         }
         float delta[2][8];
@@ -1151,7 +1208,7 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo&
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     out[e] += bias[e] + delta[i][e];
-                Vec8<T>::store_buf(yb, (uint32_t)(row * a.ldy + f) * E, out);
+                Vec8<T>::store_buf(yb, (uint32_t)(ym(row) * a.ldy + f) * E, out);
             }
         }
     }
@@ -1160,10 +1217,9 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs& a, const TileInfo&
 // One workgroup per (token tile, feature tile); the feature tile lies in one
 // slice.  NH = R / 16 when the MFMA path may run (bf16, R <= 64, slice widths
 // multiple of 32); NH = 0 builds the VALU path alone.  MODE as for the shrink.
-template <typename T, int NH, int MODE>
+template <typename T, int NH, int MODE, bool GATHER>
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
 {
-    constexpr int E = sizeof(T);
     extern __shared__ float smem[];
     float* us = smem;                                             // [kTileM][R]
     float4* part = reinterpret_cast<float4*>(us + kTileM * a.R);  // [kThreads]
@@ -1182,29 +1238,30 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
         return;
     const int f0 = ftile * a.ft;
     const int ucol0 = slice_of(a, f0) * a.R;
-    const Buf yb(reinterpret_cast<const T*>(a.y) + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * E));
+    const RowMap<GATHER> ym{a.r.rows, ti.t0, ti.n, a.r.nrows};
+    const Buf yb = ym.buf(reinterpret_cast<const T*>(a.y), a.ldy);
     // rank 16 stages y and B in LDS; ranks 32 and 64 stage B alone and keep y
     // in registers (an LDS tile of y as well would cut the workgroups per CU
     // to two or one); rank 48 reads both from memory
     if constexpr (NH > 0 && MODE == kMfmaOnly) {
         if constexpr (NH == 1)
-            expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds, bls);
+            expand_mfma<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, ylds, blds, bls);
         else if constexpr (NH == 2 || NH == 4)
-            expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds, bls);
+            expand_mfma_lb<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, ylds, bls);
         else
-            expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part, bls);
+            expand_mfma_reg<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, bls);
     } else if constexpr (NH > 0 && MODE == kMixed) {
         if (ti.glen > a.valu_max) {
             if constexpr (NH == 1)
-                expand_mfma<NH>(a, ti, f0, yb, ucol0, us, part, ylds, blds, bls);
+                expand_mfma<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, ylds, blds, bls);
             else if constexpr (NH == 2 || NH == 4)
-                expand_mfma_lb<NH>(a, ti, f0, yb, ucol0, us, part, ylds, bls);
+                expand_mfma_lb<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, ylds, bls);
             else
-                expand_mfma_reg<NH>(a, ti, f0, yb, ucol0, us, part, bls);
+                expand_mfma_reg<NH, GATHER>(a, ti, f0, yb, ym, ucol0, us, part, bls);
         } else
-            expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
+            expand_valu<T, GATHER>(a, ti, f0, yb, ym, ucol0, us, part);
     } else {
-        expand_valu<T>(a, ti, f0, yb, ucol0, us, part);
+        expand_valu<T, GATHER>(a, ti, f0, yb, ym, ucol0, us, part);
     }
 }
 
@@ -1276,7 +1333,7 @@ constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x
 
 // HOSTT: the tile comes from the host-built table tt (entries with n = 0
 // pad the grid), else from locate_tile over the routing.
-template <int NH, int STEPS, bool XLDS, bool HOSTT>
+template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
     constexpr int R = 16 * NH;
@@ -1333,8 +1390,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const int np = a.F >> 5;
     const bool pair = w < np;
     const bool tok = l16 < ti.n;
-    const Buf yb(a.y + (size_t)ti.t0 * a.ldy, (uint32_t)(ti.n * a.ldy * 2));
-    const uint32_t yoff = (pair && tok) ? (uint32_t)(l16 * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
+    const RowMap<GATHER> rm{a.r.rows, ti.t0, ti.n, a.r.nrows};
+    const uint32_t trow = rm(l16);  // the buffer row of this lane's token
+    const Buf yb = rm.buf(a.y, a.ldy);
+    const uint32_t yoff = (pair && tok) ? (uint32_t)(trow * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
     const uint4 yraw = yb.ld16(yoff);
     // the wave's 8 bias values, read with y (zero without a bias)
     const Buf biasb(a.bias + (size_t)ti.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
@@ -1352,12 +1411,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 
     // --- u partial over the wave's K range: x rows as M, A rows as N.  K
     // positions past the wave's range read as zero (offset kOOB).
-    const Buf xb(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));  // rows >= n read zero
+    const Buf xb = rm.buf(a.x, a.ldx);  // rows >= n read zero
     // the slice's NH blocks of the tiled A: one step of one block is a 1 KB run
     const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)sl * R * a.in_f, live * (uint32_t)(R * a.in_f * 2));
     const int kw0 = w * a.wave_steps * 32;
     const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
-    const uint32_t xrow = (uint32_t)(l16 * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
+    const uint32_t xrow = (uint32_t)(trow * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
     f32x4_t acc[NH];
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb)
@@ -1367,7 +1426,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
         char* xw = smem + w * kXLdsWaveBytes;
         {
             const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
-            const Buf xv(a.x + (size_t)ti.t0 * a.ldx, (uint32_t)(ti.n * a.ldx * 2));
+            const Buf xv = rm.buf(a.x, a.ldx);
 #pragma unroll
             for (int i = 0; i < kXLdsSteps; ++i) {
                 const int row = 2 * i + h;
@@ -1377,7 +1436,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
                 const int kc = kk < kw1 ? kk : kw0;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
-                    (int)((rr * a.ldx + kc) * 2), 0, 0, 0);
+                    (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
             }
         }
         uint4 ar[kXLdsSteps][NH];
@@ -1507,27 +1566,34 @@ int valu_max_for(int path, bool mfma_ok, int dflt_auto)
     return dflt_auto;
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool G>
 hipError_t launch_shrink_mode(const ShrinkArgs& a, int nb, int grid, hipStream_t st)
 {
     switch (nb) {
-    case 1: hipLaunchKernelGGL((shrink_kernel<T, 1, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((shrink_kernel<T, 2, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((shrink_kernel<T, 3, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((shrink_kernel<T, 4, MODE>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((shrink_kernel<T, 1, MODE, G>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_kernel<T, 2, MODE, G>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((shrink_kernel<T, 3, MODE, G>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_kernel<T, 4, MODE, G>), dim3(grid), dim3(kThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_shrink(bool bf16, int mode, const ShrinkArgs& a, int nb, int grid, hipStream_t st)
+template <bool G>
+hipError_t launch_shrink_g(bool bf16, int mode, const ShrinkArgs& a, int nb, int grid, hipStream_t st)
 {
     if (!bf16)
-        return launch_shrink_mode<float, kValuOnly>(a, nb, grid, st);
+        return launch_shrink_mode<float, kValuOnly, G>(a, nb, grid, st);
     if (mode == kMfmaOnly)
-        return launch_shrink_mode<uint16_t, kMfmaOnly>(a, nb, grid, st);
+        return launch_shrink_mode<uint16_t, kMfmaOnly, G>(a, nb, grid, st);
     if (mode == kValuOnly)
-        return launch_shrink_mode<uint16_t, kValuOnly>(a, nb, grid, st);
-    return launch_shrink_mode<uint16_t, kMixed>(a, nb, grid, st);
+        return launch_shrink_mode<uint16_t, kValuOnly, G>(a, nb, grid, st);
+    return launch_shrink_mode<uint16_t, kMixed, G>(a, nb, grid, st);
+}
+
+hipError_t launch_shrink(bool bf16, int mode, const ShrinkArgs& a, int nb, int grid, hipStream_t st)
+{
+    return a.r.rows ? launch_shrink_g<true>(bf16, mode, a, nb, grid, st)
+                    : launch_shrink_g<false>(bf16, mode, a, nb, grid, st);
 }
 
 // Path mode of a launch: forced paths map to one variant; AUTO with a host
@@ -1589,6 +1655,13 @@ lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path
     const bool host = rt->host_lora_ids && rt->host_grouped_offsets && G <= LORA_MAX_HOST_GROUPS;
     if (end > 0 && G > 0 && !host && (!rt->lora_ids || !rt->grouped_offsets))
         return LORA_ERR_INVALID_ARGUMENT;
+    if (rt->token_rows) {
+        // per-token routing: x and y hold num_rows rows in the caller's order
+        if (rt->num_rows < end || rt->num_rows > 2147483647LL)
+            return LORA_ERR_INVALID_ARGUMENT;
+        r.rows = rt->token_rows;
+        r.nrows = (uint32_t)rt->num_rows;
+    }
     if (host) {
         const int32_t* o = rt->host_grouped_offsets;
         if (o[0] != 0 || o[G] != end)
@@ -1649,6 +1722,32 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
 
 bool nh_possible(const Common& c, const ExpandArgs& a) { return expand_mfma_ok(c) && a.valu_max < kTileM; }
 
+template <bool G>
+void launch_expand(bool bf16, int nh, int mode, dim3 g, dim3 b, size_t lds, hipStream_t s, const ExpandArgs& a)
+{
+#define LORA_EXPAND_NH(NHV)                                                                       \
+    if (mode == kMfmaOnly)                                                                        \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMfmaOnly, G>), g, b, lds, s, a);        \
+    else if (mode == kValuOnly)                                                                   \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly, G>), g, b, lds, s, a);          \
+    else                                                                                          \
+        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMixed, G>), g, b, lds, s, a);
+    if (!bf16) {
+        hipLaunchKernelGGL((expand_kernel<float, 0, kValuOnly, G>), g, b, lds, s, a);
+    } else if (nh == 1) {
+        LORA_EXPAND_NH(1)
+    } else if (nh == 2) {
+        LORA_EXPAND_NH(2)
+    } else if (nh == 3) {
+        LORA_EXPAND_NH(3)
+    } else if (nh == 4) {
+        LORA_EXPAND_NH(4)
+    } else {
+        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly, G>), g, b, lds, s, a);
+    }
+#undef LORA_EXPAND_NH
+}
+
 lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, const void* B_stack,
                          const void* bias, void* y, int64_t ldy, int32_t path, hipStream_t s)
 {
@@ -1687,27 +1786,10 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
                        (nh && bias ? (size_t)kExpandCols * sizeof(uint16_t) : 0);
     const dim3 g((unsigned)grid), b(kThreads);
     const int mode = nh ? pick_mode(path, true, a.valu_max, c.r) : kValuOnly;
-#define LORA_EXPAND_NH(NHV)                                                                       \
-    if (mode == kMfmaOnly)                                                                        \
-        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMfmaOnly>), g, b, lds, s, a);           \
-    else if (mode == kValuOnly)                                                                   \
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly>), g, b, lds, s, a);             \
-    else                                                                                          \
-        hipLaunchKernelGGL((expand_kernel<uint16_t, NHV, kMixed>), g, b, lds, s, a);
-    if (!c.bf16) {
-        hipLaunchKernelGGL((expand_kernel<float, 0, kValuOnly>), g, b, lds, s, a);
-    } else if (nh == 1) {
-        LORA_EXPAND_NH(1)
-    } else if (nh == 2) {
-        LORA_EXPAND_NH(2)
-    } else if (nh == 3) {
-        LORA_EXPAND_NH(3)
-    } else if (nh == 4) {
-        LORA_EXPAND_NH(4)
-    } else {
-        hipLaunchKernelGGL((expand_kernel<uint16_t, 0, kValuOnly>), g, b, lds, s, a);
-    }
-#undef LORA_EXPAND_NH
+    if (c.r.rows)
+        launch_expand<true>(c.bf16, nh, mode, g, b, lds, s, a);
+    else
+        launch_expand<false>(c.bf16, nh, mode, g, b, lds, s, a);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
@@ -1833,11 +1915,16 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
     const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
     const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
+    const bool gather = c.r.rows != nullptr;
 #define LORA_FUSED(NH, ST, XL)                                                             \
-    if (hostt)                                                                             \
-        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, true>), g, blk, 0, s, a);       \
+    if (hostt && gather)                                                                   \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, true, true>), g, blk, 0, s, a); \
+    else if (hostt)                                                                        \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, true, false>), g, blk, 0, s, a); \
+    else if (gather)                                                                       \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, false, true>), g, blk, 0, s, a); \
     else                                                                                   \
-        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, false>), g, blk, 0, s, a);
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, XL, false, false>), g, blk, 0, s, a);
     if (c.fs.R == 16) {
         if (xlds) {
             LORA_FUSED(1, 8, true)
@@ -1860,6 +1947,13 @@ bool row_ok(int64_t ld, int64_t width, int elem)
     return ld >= width && (ld * elem) % 16 == 0 && ld * elem <= kMaxRowBytes;
 }
 
+// Under per-token routing one buffer resource spans all of x or y, and row
+// num_rows is the out-of-range row: every offset must fit 32 bits.
+bool rows_fit(const Common& c, int64_t ld)
+{
+    return !c.r.rows || ((int64_t)c.r.nrows + 1) * ld * c.fs.elem <= 0xFFFFFFFFLL;
+}
+
 }  // namespace
 }  // namespace lora
 
@@ -1879,7 +1973,7 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
         return LORA_ERR_INVALID_ARGUMENT;
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
-    if (!x || !A_stack || !u || !row_ok(ldx, c.fs.in_f, c.fs.elem) || !aligned16(x) ||
+    if (!x || !A_stack || !u || !row_ok(ldx, c.fs.in_f, c.fs.elem) || !rows_fit(c, ldx) || !aligned16(x) ||
         !aligned16(A_stack) || !aligned16(u))
         return LORA_ERR_INVALID_ARGUMENT;
     const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
@@ -1913,7 +2007,7 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
         return LORA_ERR_INVALID_ARGUMENT;
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
-    if (!u || !B_stack || !y || !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(u) ||
+    if (!u || !B_stack || !y || !row_ok(ldy, c.fs.out_f, c.fs.elem) || !rows_fit(c, ldy) || !aligned16(u) ||
         !aligned16(B_stack) || !aligned16(y) || !aligned16(bias_stack))
         return LORA_ERR_INVALID_ARGUMENT;
     return run_expand(c, u, 0, 1, B_stack, bias_stack, y, ldy, path, reinterpret_cast<hipStream_t>(stream));
@@ -1934,7 +2028,8 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
     if (c.r.end == 0 || c.r.G == 0)
         return LORA_OK;
     if (!x || !A_stack || !B_stack || !y || !workspace || !row_ok(ldx, c.fs.in_f, c.fs.elem) ||
-        !row_ok(ldy, c.fs.out_f, c.fs.elem) || !aligned16(x) || !aligned16(y) || !aligned16(A_stack) ||
+        !row_ok(ldy, c.fs.out_f, c.fs.elem) || !rows_fit(c, ldx) || !rows_fit(c, ldy) || !aligned16(x) ||
+        !aligned16(y) || !aligned16(A_stack) ||
         !aligned16(B_stack) || !aligned16(workspace) || !aligned16(bias_stack))
         return LORA_ERR_INVALID_ARGUMENT;
     const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
