@@ -17,6 +17,11 @@ padded to 16, 25% base requests, bf16 data with fp32 accumulation, run over
 Output: one JSON line (rank 0).  `value` = LoRA-routed tokens x layers per
 second (tokens through one layer's q/k/v/o delta per second).
 
+Options that change the work: --bias (every adapter also carries a LoRA
+bias), --token-routing (per-token routing: x and y stay in token order and
+the kernels gather and scatter rows through the sorted token indices, built
+and uploaded every step), --workload, --api, --path.
+
 Phases:
   1. timed steps, the layer loop captured once in a HIP graph and replayed
      (host routing + routing upload stay eager every step);
@@ -51,6 +56,9 @@ KERNEL_SRC = os.path.join(ROOT, "segmented_rank_gemv_amd", "csrc", "lora_sgmv.hi
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+UPLOAD_PIECE = 4096  # int32 entries per host-to-device copy of the token indices
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -63,6 +71,9 @@ def parse():
                    help="delta: lora_sgmv_delta per family; split: lora_sgmv_shrink + lora_sgmv_expand")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--bias", action="store_true", help="every adapter also carries a LoRA bias per projection")
+    p.add_argument("--token-routing", action="store_true",
+                   help="per-token routing: x and y stay in token order; each step builds the token "
+                        "routing (lora_build_token_routing) and uploads the sorted token indices")
     p.add_argument("--device-routing", action="store_true",
                    help="kernels read the routing from device memory only (no host copies)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -187,9 +198,15 @@ def main():
 
     # routing once to lay the batch out in sorted order (the serving layer
     # sorts its batch once; the timed steps still route on the host)
-    rt0 = srg.lora_build_routing(slots, offsets, L)
+    token_slot = np.repeat(slots, lengths).astype(np.int32)
+    if args.token_routing:
+        # the batch stays in token order; the kernels gather and scatter rows
+        rt0 = srg.lora_build_token_routing(token_slot, L)
+        order = np.arange(T)
+    else:
+        rt0 = srg.lora_build_routing(slots, offsets, L)
+        order = np.concatenate([np.arange(offsets[p], offsets[p + 1]) for p in rt0["perm"]])
     end, G = rt0["end"], rt0["num_groups"]
-    order = np.concatenate([np.arange(offsets[p], offsets[p + 1]) for p in rt0["perm"]])
     fam_shape = {fm[0]: srg.lora_family_shape(dims, fm[0]) for fm in FAMS}
     proj_desc = "gate/up/down" if mlp else "q/k/v/o"
     log(f"workload={w.name} T={T} end={end} G={G} layers={n_layers}")
@@ -247,12 +264,16 @@ def main():
     offs_pin = torch.zeros(L + 1, dtype=torch.int32).pin_memory()
     # the routing the kernels see: device arrays (refreshed every step) plus,
     # unless --device-routing, host copies passed as launch arguments
+    rows_dev = torch.zeros(max(end, 1), dtype=torch.int32, device=dev)
+    rows_pin = torch.zeros(max(end, 1), dtype=torch.int32).pin_memory()
     routing = srg.LoraRouting(ids_dev, offs_dev, G, end,
                               None if args.device_routing else rt0["lora_ids"],
-                              None if args.device_routing else rt0["grouped_offsets"])
+                              None if args.device_routing else rt0["grouped_offsets"],
+                              rows_dev if args.token_routing else None, T)
 
     def route_and_upload():
-        rt = srg.lora_build_routing(slots, offsets, L)
+        rt = (srg.lora_build_token_routing(token_slot, L) if args.token_routing
+              else srg.lora_build_routing(slots, offsets, L))
         assert rt["end"] == end and rt["num_groups"] == G
         assert np.array_equal(rt["lora_ids"], rt0["lora_ids"])
         assert np.array_equal(rt["grouped_offsets"], rt0["grouped_offsets"])
@@ -260,6 +281,13 @@ def main():
         offs_pin[:G + 1].copy_(torch.from_numpy(rt["grouped_offsets"]))
         ids_dev.copy_(ids_pin, non_blocking=True)
         offs_dev.copy_(offs_pin, non_blocking=True)
+        if args.token_routing:
+            assert np.array_equal(rt["token_indices_sorted"], rt0["token_indices_sorted"])
+            rows_pin[:end].copy_(torch.from_numpy(rt["token_indices_sorted"][:end]))
+            # in pieces of 16 KB: a larger pinned copy blocks the host until
+            # the stream drains (measured), which would serialise the steps
+            for c0 in range(0, max(end, 1), UPLOAD_PIECE):
+                rows_dev[c0:c0 + UPLOAD_PIECE].copy_(rows_pin[c0:c0 + UPLOAD_PIECE], non_blocking=True)
 
     if args.api == "delta":
         KINDS = tuple("delta_" + fm[1] for fm in FAMS)
@@ -315,8 +343,12 @@ def main():
             all_layers()
         torch.cuda.synchronize()
 
+    host_route_s = [0.0]
+
     def step():
+        t0 = time.perf_counter()
         route_and_upload()
+        host_route_s[0] += time.perf_counter() - t0
         if graph is not None:
             graph.replay()
         else:
@@ -327,6 +359,7 @@ def main():
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        host_route_s[0] = 0.0
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step()
@@ -524,6 +557,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "host_routing_us_per_step": 1e6 * host_route_s[0] / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -535,6 +569,7 @@ def main():
                    "tokens": T, "lora_tokens": end, "groups": G, "max_num_loras": L,
                    "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,
                    "api": args.api, "routing": "device" if args.device_routing else "host+device",
+                   "token_routing": bool(args.token_routing),
                    "hip_graph": graph is not None, "lora_bias": bool(args.bias)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
