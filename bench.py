@@ -370,12 +370,24 @@ def main():
 
     # ---- phase 2: per-call durations with HIP events on the launch stream.
     # For every call kind the same call runs over all layers back to back
-    # (cold data, as in the step) between one pair of events; a bounded spin
-    # kernel (torch.cuda._sleep) runs first so that the host has queued the
-    # whole sequence before the GPU reaches it, so the events time the
-    # kernels and not the host's launch rate.
+    # (cold data, as in the step) between one pair of events.  With graphs
+    # (the default, as in the timed step) each kind's sequence is one
+    # captured graph, so the events time the kernels as the step launches
+    # them; without, a bounded spin kernel (torch.cuda._sleep) runs first so
+    # that the host has queued the whole eager sequence before the GPU
+    # reaches it, so the events time the kernels and not the host's launch
+    # rate.
     ev_reps = max(1, min(args.steps, 20))
     total_ms = {k: 0.0 for k in KINDS}
+    kind_graphs = {}
+    if graph is not None:
+        for kind in KINDS:
+            kg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(kg, stream=stream):
+                for ly in layers:
+                    call(kind, ly)
+            kind_graphs[kind] = kg
+        torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         route_and_upload()
         torch.cuda.synchronize()
@@ -396,8 +408,11 @@ def main():
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda._sleep(spin)
                 a.record()
-                for ly in layers:
-                    call(kind, ly)
+                if kind in kind_graphs:
+                    kind_graphs[kind].replay()
+                else:
+                    for ly in layers:
+                        call(kind, ly)
                 b.record()
                 torch.cuda.synchronize()
                 total_ms[kind] += a.elapsed_time(b)

@@ -1314,6 +1314,7 @@ struct FusedArgs {
     int soff[5];
     int nft[4];      // feature tiles per slice
     int nf;          // feature tiles per token tile
+    int krot;        // nonzero: wave w takes K range (w + feature tile) mod waves
     RouteArgs r;
     TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
     int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT)
@@ -1414,7 +1415,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const Buf xb = rm.buf(a.x, a.ldx);  // rows >= n read zero
     // the slice's NH blocks of the tiled A: one step of one block is a 1 KB run
     const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)sl * R * a.in_f, live * (uint32_t)(R * a.in_f * 2));
-    const int kw0 = w * a.wave_steps * 32;
+    // K range of this wave.  With krot the feature tiles of one token tile
+    // start on different K ranges, so the workgroups that read the same x
+    // and A lines do not ask for them in the same order; the partial sums are
+    // still added in K-range order, so the result does not depend on it.
+    const int kr = a.krot ? (w + ftile) & (kFusedWaves - 1) : w;
+    const int kw0 = kr * a.wave_steps * 32;
     const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
     const uint32_t xrow = (uint32_t)(trow * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
     f32x4_t acc[NH];
@@ -1494,7 +1500,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     for (int nb = 0; nb < NH; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            part[(w * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
+            part[(kr * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
     __syncthreads();
     for (int e = threadIdx.x; e < kFusedTileM * R; e += kFusedThreads) {
         float v = part[e];
@@ -1844,6 +1850,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / F : 0;
         a.nf += a.nft[sl];
     }
+    a.krot = env_int("LORA_SGMV_FUSED_KROT", 1);
     const int steps = (c.fs.in_f + 31) / 32;
     a.wave_steps = (steps + kFusedWaves - 1) / kFusedWaves;
     a.r = c.r;
