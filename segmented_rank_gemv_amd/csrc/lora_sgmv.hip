@@ -33,6 +33,7 @@
 // results.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <atomic>
 #include <stdlib.h>
 #include <string.h>
 
@@ -1553,6 +1554,22 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device, queried once per device.
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Default VALU/MFMA split (tokens per tile); overridable for tuning through
 // LORA_SGMV_VALU_MAX_SHRINK / LORA_SGMV_VALU_MAX_EXPAND.
 int env_int(const char* name, int dflt)
@@ -1839,17 +1856,22 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     a.n_s = c.fs.n_s;
     for (int i = 0; i < 5; ++i)
         a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
-    // feature tile: the largest power of two <= kFusedMaxFeat dividing every slice width
-    int F = kFusedMaxFeat;
+    // feature tile: the largest power of two <= kFusedMaxFeat dividing every
+    // slice width (narrowed below once the tile count is known)
+    const int feat_env = env_int("LORA_SGMV_FUSED_FEAT", 0);
+    int F = feat_env > 0 ? std::min(std::max(feat_env, 32), kFusedMaxFeat) : kFusedMaxFeat;
     for (int sl = 0; sl < c.fs.n_s; ++sl)
         while (c.fs.widths[sl] % F)
             F >>= 1;
-    a.F = F;
-    a.nf = 0;
-    for (int sl = 0; sl < 4; ++sl) {
-        a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / F : 0;
-        a.nf += a.nft[sl];
-    }
+    auto set_feat = [&](int f) {
+        a.F = f;
+        a.nf = 0;
+        for (int sl = 0; sl < 4; ++sl) {
+            a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / f : 0;
+            a.nf += a.nft[sl];
+        }
+    };
+    set_feat(F);
     a.krot = env_int("LORA_SGMV_FUSED_KROT", 1);
     const int steps = (c.fs.in_f + 31) / 32;
     a.wave_steps = (steps + kFusedWaves - 1) / kFusedWaves;
@@ -1862,10 +1884,9 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     } else {
         tiles = ((int64_t)c.r.end + kFusedTileM - 1) / kFusedTileM + c.r.G;
     }
-    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds * a.nf;
-    if (grid == 0)
+    if (tiles == 0)
         return LORA_OK;
-    if (grid > 2147483647LL || (tiles + kXcds - 1) / kXcds > 65535)
+    if ((int64_t)(tiles + kXcds - 1) / kXcds * kXcds * a.nf > 2147483647LL || (tiles + kXcds - 1) / kXcds > 65535)
         return LORA_ERR_INVALID_ARGUMENT;
     // tile table from the host routing: the tiles of locate_tile<kFusedTileM,
     // true> (each group cut into ceil(len / 16) near-equal tiles)
@@ -1910,6 +1931,24 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         } else {
             rows = (tiles + kXcds - 1) / kXcds;
         }
+    }
+    // Every workgroup reads its token tile's x rows and its slice's A rows
+    // whatever its feature tile, and that read is most of its time; halving
+    // the feature tile doubles the workgroups without changing that read.
+    // So the tile is halved (down to 128 features) only while each XCD still
+    // runs at most one workgroup per compute unit: then the extra
+    // workgroups land on idle units and each one's y and B share shrinks.
+    if (feat_env <= 0) {
+        const int per_xcd = device_cus() / kXcds;
+        while (F > 128) {
+            int nf2 = 0;
+            for (int sl = 0; sl < c.fs.n_s; ++sl)
+                nf2 += c.fs.widths[sl] / (F / 2);
+            if (rows * nf2 > per_xcd || (hostt && nf2 > kFusedHostFt))
+                break;
+            F /= 2;
+        }
+        set_feat(F);
     }
     if (hostt) {
         int ft = 0;

@@ -377,3 +377,39 @@ def test_host_side_argument_errors_launch_nothing():
         srg.lora_sgmv_expand(d32, srg.FAMILY_O, u, A, rt, x, srg.PATH_MFMA)
     assert e.value.code == 1
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["decode", "stack_decode"])
+def test_fused_launch_shapes_bit_identical(name, monkeypatch):
+    """The one-kernel delta's launch choices do not change its arithmetic:
+    every feature tile width (128, 256 or 512 features per workgroup, or the
+    launcher's own pick) and the wave K-range rotation on or off give the same
+    bits, and each of them matches the oracle.  The partial sums over the K
+    ranges are added in K-range order whatever wave computed them, and each
+    output feature's expand is the same sum whatever its tile.  stack_decode:
+    the rank-32 stack adapters on a decode-shaped batch (one token per request)."""
+    if name == "decode":
+        w, lengths, slots, stacks, acts, ref = workload_case("decode")
+    else:
+        w = synth.get_workload("stack")
+        rng = np.random.default_rng(11)
+        lengths = np.ones(160, np.int64)
+        slots = np.where(rng.random(160) < 0.2, -1, rng.integers(0, w.max_num_loras, 160)).astype(np.int32)
+        stacks = pack_stacks(w, 3, synth.draw_ranks(w))
+        acts = synth.draw_activations(w, 3, int(lengths.sum()))
+        ref = oracle_layer(w, stacks, lengths, slots, acts)
+    outs = {}
+    for feat in ("", "512", "256", "128"):
+        for krot in ("1", "0"):
+            monkeypatch.setenv("LORA_SGMV_FUSED_FEAT", feat)
+            monkeypatch.setenv("LORA_SGMV_FUSED_KROT", krot)
+            log(f"[fused-shapes] workload={name} feat={feat or 'auto'} krot={krot}")
+            gl = GpuLayer(w, stacks, lengths, slots, acts)
+            gl.run(srg.PATH_FUSED, fused=True)
+            ey, _ = compare(w, gl, ref, check_u=False)
+            assert ey <= TOL[w.dtype], (feat, krot, ey)
+            outs[(feat, krot)] = (gl.y_arrival("y_qkv"), gl.y_arrival("y_o"))
+    first = outs[("", "1")]
+    for key, (yq, yo) in outs.items():
+        assert np.array_equal(yq.view(np.uint32), first[0].view(np.uint32)), key
+        assert np.array_equal(yo.view(np.uint32), first[1].view(np.uint32)), key
