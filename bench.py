@@ -157,7 +157,7 @@ def main():
         summarize_traffic(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark measures one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
         sys.exit(2)
 

@@ -51,14 +51,16 @@ def workload_case(name, layer=0):
     return _CACHE[key]
 
 
-@pytest.mark.parametrize("api", ["split", "delta", "delta_reduce", "split_devroute"])
+@pytest.mark.parametrize("api", ["split", "delta", "delta_reduce", "delta_nofold", "split_devroute"])
 @pytest.mark.parametrize("path", list(DELTA_PATHS))
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
 def test_full_workload_parity(name, path, api, monkeypatch):
     """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
     lora_sgmv_delta (AUTO takes the one-kernel path on decode batches);
     delta_reduce: lora_sgmv_delta on the two-kernel path with its slabs folded
-    by the reduce kernel before the expand; split_devroute: split with the
+    by the reduce kernel before the expand (by default only batches of 2048
+    or more LoRA tokens fold); delta_nofold: the same path with the expand
+    reading every slab itself; split_devroute: split with the
     routing read from the device arrays only.  path fused: lora_sgmv_delta
     forced onto the one-kernel path."""
     w, lengths, slots, stacks, acts, ref = workload_case(name)
@@ -68,8 +70,8 @@ def test_full_workload_parity(name, path, api, monkeypatch):
         pytest.skip("the one-kernel path exists for lora_sgmv_delta only")
     if path == "fused" and not fused_applies(w):
         pytest.skip("one-kernel path needs bf16 and rank 16 or 32 (error path tested separately)")
-    if api == "delta_reduce":
-        monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1")
+    if api in ("delta_reduce", "delta_nofold"):
+        monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1" if api == "delta_reduce" else "0")
         monkeypatch.setenv("LORA_SGMV_FUSED_MAX", "0")
     log(f"[parity] workload={name} path={path} api={api} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts)
