@@ -454,6 +454,36 @@ def main():
     value = end * n_layers / (ms_per_step * 1e-3)
     e2e_gbs = fam_bytes * n_layers / (ms_per_step * 1e-3) / 1e9
 
+    # ---- reference streams (outside the step): what plain device kernels
+    # reach on this GPU, beside the 8 TB/s nameplate -- an in-place add over
+    # 1 GiB of bf16 (read + write, like the expand's y) and a row-wise max
+    # over the same bytes (read only, like the shrink's x)
+    stream_ref = None
+    if not args.counters:
+        big = torch.empty(2**29, dtype=torch.bfloat16, device=dev).normal_()
+        rows2d = big.view(-1, 4096)
+
+        def ev_time(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record()
+            for _ in range(reps):
+                fn()
+            eb.record()
+            torch.cuda.synchronize()
+            return ea.elapsed_time(eb) * 1e-3 / reps
+
+        nbytes = big.numel() * 2
+        t_rw = ev_time(lambda: big.add_(1.0))
+        t_rd = ev_time(lambda: rows2d.amax(dim=1))
+        stream_ref = {"inplace_add_GBps": 2 * nbytes / t_rw / 1e9, "row_max_read_GBps": nbytes / t_rd / 1e9,
+                      "bytes": nbytes}
+        del big, rows2d
+        torch.cuda.empty_cache()
+        log(f"reference streams: in-place add {stream_ref['inplace_add_GBps']:.0f} GB/s, "
+            f"row max read {stream_ref['row_max_read_GBps']:.0f} GB/s")
+
     # ---- adapter activation (outside the step): the slot cache's decisions
     # for a stream of batches over twice as many adapters as slots, and the
     # host-to-device writes of one adapter into one slot of every layer
@@ -593,6 +623,7 @@ def main():
         "calls": {k: {"avg_us": avg_us[k], "bytes": kbytes[k], "flops": kflops[k],
                       "GBps": kbytes[k] / (avg_us[k] * 1e-6) / 1e9} for k in KINDS},
         "end_to_end_GBps": e2e_gbs,
+        "stream_reference": stream_ref,
         "pack_ms_per_adapter_layer": 1e3 * t_pack / max(n_pack, 1),
         "activation": activation,
         "cpu_baseline": cpu,

@@ -432,3 +432,50 @@ def test_memory_formula_matches_stack_sizes():
     packed = sum(a.nbytes for a in pk.values())
     want = sum(formula(1, fi, fo, R, 2, 1) for fi, fo in ((H, nq), (H, nkv), (H, nkv), (nq, H)))
     assert packed == want
+
+
+def test_delta_batch_composition_invariant_brute_force():
+    """A request's result does not depend on the rest of its batch: on the
+    tiny attention workload (5/3/4 tokens routed to slots 0, 1 and base) and on
+    a five-request variant that repeats slots and adds an empty request, every
+    non-empty subset of the requests, in every arrival order, gives each
+    request bit-for-bit the y and u it gets in the whole batch (the routing
+    sorts, groups and truncates per batch; the result must not see that)."""
+    import synth
+    w = synth.get_workload("tiny")
+    ranks = synth.draw_ranks(w)
+    A, B = [], []
+    for s in range(w.max_num_loras):
+        pk = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank,
+                                 w.dtype, int(ranks[s]), w.lora_alpha, w.use_rslora, True, "qkvo",
+                                 synth.draw_adapter(w, 0, s, int(ranks[s])))
+        A.append(pk["A_qkv"])
+        B.append(pk["B_qkv"])
+    A, B = np.stack(A), np.stack(B)
+    widths = [w.nq, w.nkv, w.nkv]
+    lengths0, slots0 = synth.draw_requests(w)
+    cases = [(np.asarray(lengths0, np.int64), np.asarray(slots0, np.int32)),
+             (np.array([2, 0, 3, 1, 4], np.int64), np.array([1, 0, -1, 1, 0], np.int32))]
+    for lengths, slots in cases:
+        offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        act = synth.draw_activations(w, 1, int(offs[-1]))
+        full = oracle.reference_family(act["x_qkv"], act["y_qkv"], offs, slots, A, B, widths,
+                                       w.max_lora_rank, w.dtype)
+        n = len(lengths)
+        for k in range(1, n + 1):
+            for sub in itertools.permutations(range(n), k):
+                sl = np.array([slots[i] for i in sub], np.int32)
+                ln = np.array([lengths[i] for i in sub], np.int64)
+                so = np.concatenate([[0], np.cumsum(ln)]).astype(np.int64)
+                rows = np.concatenate([np.arange(offs[i], offs[i + 1]) for i in sub]).astype(np.int64)
+                part = oracle.reference_family(act["x_qkv"][rows], act["y_qkv"][rows], so, sl, A, B,
+                                               widths, w.max_lora_rank, w.dtype)
+                for j, i in enumerate(sub):
+                    r_sub, y_sub, u_sub = part[j]
+                    r_all, y_all, u_all = full[i]
+                    assert np.array_equal(r_sub, r_all)
+                    assert np.array_equal(y_sub.view(np.int64), y_all.view(np.int64)), (sub, i)
+                    if u_all is None:
+                        assert u_sub is None
+                    else:
+                        assert np.array_equal(u_sub.view(np.int64), u_all.view(np.int64)), (sub, i)
