@@ -1316,9 +1316,13 @@ struct FusedArgs {
     int nft[4];      // feature tiles per slice
     int nf;          // feature tiles per token tile
     int krot;        // nonzero: wave w takes K range (w + feature tile) mod waves
+    int kc;          // SHRINK: K range of one split (a multiple of 32)
+    float* slabs;    // SHRINK: fp32 slab s at slabs + s * slab, each [end][C]
+    int64_t slab;
     RouteArgs r;
     TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
-    int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT)
+    int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT);
+                                    // SHRINK: (slice, K split)
 };
 
 // STEPS = K steps a wave keeps in flight per batch (register budget).
@@ -1335,9 +1339,14 @@ constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x
 
 // HOSTT: the tile comes from the host-built table tt (entries with n = 0
 // pad the grid), else from locate_tile over the routing.
-template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER>
+// SHRINK: the shrink half alone, with K split over workgroups.  Workgroup
+// (tile, slice, split s) sums x . A over K range [s kc, (s + 1) kc) of its
+// slice and writes the tile's rows of slab s; the expand kernel adds the
+// slabs in split order.  Nothing of y or B is read.
+template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER, bool SHRINK = false>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
+    static_assert(!SHRINK || HOSTT, "the shrink-only launch uses the host tile table");
     constexpr int R = 16 * NH;
     constexpr int kPartBytes = kFusedWaves * kFusedTileM * R * 4;
     constexpr int kXBytes = XLDS ? kFusedWaves * kXLdsWaveBytes : 0;
@@ -1396,10 +1405,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const uint32_t trow = rm(l16);  // the buffer row of this lane's token
     const Buf yb = rm.buf(a.y, a.ldy);
     const uint32_t yoff = (pair && tok) ? (uint32_t)(trow * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
-    const uint4 yraw = yb.ld16(yoff);
+    const uint4 yraw = SHRINK ? make_uint4(0u, 0u, 0u, 0u) : yb.ld16(yoff);
     // the wave's 8 bias values, read with y (zero without a bias)
     const Buf biasb(a.bias + (size_t)ti.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
-    const uint4 braw_bias = biasb.ld16(pair ? (uint32_t)(32 * w + 8 * q) * 2 : kOOB);
+    const uint4 braw_bias = SHRINK ? make_uint4(0u, 0u, 0u, 0u) : biasb.ld16(pair ? (uint32_t)(32 * w + 8 * q) * 2 : kOOB);
     // B rows as the M operand, permuted: row i of block h is feature
     // 32 w + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
     const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
@@ -1409,7 +1418,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int kh = 0; kh < NH; ++kh)
-            bfr[h][kh] = bb.ld16(pair ? (uint32_t)((32 * w + mrow + 4 * h) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+            bfr[h][kh] = SHRINK ? make_uint4(0u, 0u, 0u, 0u)
+                                : bb.ld16(pair ? (uint32_t)((32 * w + mrow + 4 * h) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
 
     // --- u partial over the wave's K range: x rows as M, A rows as N.  K
     // positions past the wave's range read as zero (offset kOOB).
@@ -1421,8 +1431,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     // and A lines do not ask for them in the same order; the partial sums are
     // still added in K-range order, so the result does not depend on it.
     const int kr = a.krot ? (w + ftile) & (kFusedWaves - 1) : w;
-    const int kw0 = kr * a.wave_steps * 32;
-    const int kw1 = min(kw0 + a.wave_steps * 32, a.in_f);
+    // SHRINK: this workgroup's split of K (f0 holds the split index)
+    const int kbase = SHRINK ? f0 * a.kc : 0;
+    const int kend = SHRINK ? min(kbase + a.kc, a.in_f) : a.in_f;
+    const int kw0 = kbase + kr * a.wave_steps * 32;
+    const int kw1 = min(kw0 + a.wave_steps * 32, kend);
     const uint32_t xrow = (uint32_t)(trow * a.ldx) * 2, ablk = (uint32_t)(16 * a.in_f) * 2;
     f32x4_t acc[NH];
 #pragma unroll
@@ -1440,7 +1453,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
                 const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
                 const int kk = kw0 + 8 * c;
                 const int rr = min(row, ti.n - 1);
-                const int kc = kk < kw1 ? kk : kw0;
+                const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
                     (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
@@ -1511,6 +1524,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
         us[e] = v;
     }
     __syncthreads();
+    if constexpr (SHRINK) {
+        // the tile's rows of slab f0, columns of slice sl
+        float* dst = a.slabs + (size_t)f0 * a.slab + (size_t)ti.t0 * a.C + sl * R;
+        for (int e = threadIdx.x; e < ti.n * R; e += kFusedThreads)
+            dst[(size_t)(e / R) * a.C + e % R] = us[e];
+        return;
+    }
     if (!pair)
         return;
 
@@ -1843,10 +1863,10 @@ bool fused_auto(const Common& c)
 // 3.6 K tokens, -5 %; a 0.8 K-token mixed batch, +3 %).
 constexpr int kDeltaFoldTokens = 2048;
 
-lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void* A_stack, const void* B_stack,
-                        const void* bias, void* y, int64_t ldy, hipStream_t s)
+// The launch arguments every one-kernel launch shares.
+void fused_common_args(const Common& c, FusedArgs& a, const void* x, int64_t ldx, const void* A_stack,
+                       const void* B_stack, const void* bias, void* y, int64_t ldy)
 {
-    FusedArgs a;
     a.bias = reinterpret_cast<const uint16_t*>(bias);
     a.x = reinterpret_cast<const uint16_t*>(x);
     a.ldx = ldx;
@@ -1861,6 +1881,71 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     a.n_s = c.fs.n_s;
     for (int i = 0; i < 5; ++i)
         a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
+    a.krot = env_int("LORA_SGMV_FUSED_KROT", 1);
+    a.kc = 0;
+    a.slabs = nullptr;
+    a.slab = 0;
+    a.r = c.r;
+}
+
+// Token tiles of the one-kernel launches from the host routing: each group
+// cut into ceil(len / 16) near-equal tiles (the tiles locate_tile<kFusedTileM,
+// true> finds).
+int64_t fused_host_tiles(const Common& c)
+{
+    int64_t tiles = 0;
+    for (int g = 0; g < c.r.G; ++g)
+        tiles += (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM;
+    return tiles;
+}
+
+// The host tile table: the tiles of a group go to one XCD (tile position
+// y * kXcds + xcd), so that its A and B rows are fetched into one L2: groups,
+// largest first, each to the XCD with the fewest tiles so far.  rows gets the
+// grid height (tiles per XCD).  False when the table cannot hold the tiles.
+bool fused_tile_table(const Common& c, FusedArgs& a, int64_t& rows)
+{
+    int order[LORA_MAX_HOST_GROUPS], cnt[kXcds] = {}, xcd_of[LORA_MAX_HOST_GROUPS];
+    const bool together = env_int("LORA_SGMV_XCD_GROUPS", 1) != 0;
+    for (int g = 0; g < c.r.G; ++g)
+        order[g] = g;
+    auto gtiles = [&](int g) { return (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM; };
+    rows = (fused_host_tiles(c) + kXcds - 1) / kXcds;
+    if (together) {
+        std::stable_sort(order, order + c.r.G, [&](int p, int q) { return gtiles(p) > gtiles(q); });
+        for (int i = 0; i < c.r.G; ++i) {
+            int best = 0;
+            for (int x = 1; x < kXcds; ++x)
+                if (cnt[x] < cnt[best])
+                    best = x;
+            xcd_of[order[i]] = best;
+            cnt[best] += gtiles(order[i]);
+        }
+        rows = *std::max_element(cnt, cnt + kXcds);
+    }
+    if (rows * kXcds > kFusedHostTiles)
+        return false;
+    for (int i = 0; i < kFusedHostTiles; ++i)
+        a.tt[i] = TileEntry{0, 0, 0, 0};
+    int fill[kXcds] = {}, n = 0;
+    for (int g = 0; g < c.r.G; ++g) {
+        const int gs = c.r.k_offs[g], len = c.r.k_offs[g + 1] - gs;
+        const int gnt = gtiles(g);
+        for (int j = 0; j < gnt; ++j) {
+            const int t0 = gs + (int)(((int64_t)len * j) / gnt);
+            const int t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
+            const int pos = together ? fill[xcd_of[g]]++ * kXcds + xcd_of[g] : n++;
+            a.tt[pos] = TileEntry{t0, t1 - t0, c.r.k_ids[g], len};
+        }
+    }
+    return true;
+}
+
+lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void* A_stack, const void* B_stack,
+                        const void* bias, void* y, int64_t ldy, hipStream_t s)
+{
+    FusedArgs a;
+    fused_common_args(c, a, x, ldx, A_stack, B_stack, bias, y, ldy);
     // feature tile: the largest power of two <= kFusedMaxFeat dividing every
     // slice width (narrowed below once the tile count is known)
     const int feat_env = env_int("LORA_SGMV_FUSED_FEAT", 0);
@@ -1877,66 +1962,19 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         }
     };
     set_feat(F);
-    a.krot = env_int("LORA_SGMV_FUSED_KROT", 1);
     const int steps = (c.fs.in_f + 31) / 32;
     a.wave_steps = (steps + kFusedWaves - 1) / kFusedWaves;
-    a.r = c.r;
     // token tiles: exact count from the host routing, else a bound
-    int64_t tiles = 0;
-    if (c.r.kr) {
-        for (int g = 0; g < c.r.G; ++g)
-            tiles += (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM;
-    } else {
-        tiles = ((int64_t)c.r.end + kFusedTileM - 1) / kFusedTileM + c.r.G;
-    }
+    const int64_t tiles =
+        c.r.kr ? fused_host_tiles(c) : ((int64_t)c.r.end + kFusedTileM - 1) / kFusedTileM + c.r.G;
     if (tiles == 0)
         return LORA_OK;
     if ((int64_t)(tiles + kXcds - 1) / kXcds * kXcds * a.nf > 2147483647LL || (tiles + kXcds - 1) / kXcds > 65535)
         return LORA_ERR_INVALID_ARGUMENT;
-    // tile table from the host routing: the tiles of locate_tile<kFusedTileM,
-    // true> (each group cut into ceil(len / 16) near-equal tiles)
-    // The tiles of a group go to one XCD (tile position y * kXcds + xcd), so
-    // that its A and B rows are fetched into one L2: groups, largest first,
-    // each to the XCD with the fewest tiles so far.
     int64_t rows = (tiles + kXcds - 1) / kXcds;  // grid rows (tiles per XCD)
-    bool hostt = c.r.kr && a.nf <= kFusedHostFt;
-    if (hostt) {
-        int order[LORA_MAX_HOST_GROUPS], cnt[kXcds] = {}, xcd_of[LORA_MAX_HOST_GROUPS];
-        const bool together = env_int("LORA_SGMV_XCD_GROUPS", 1) != 0;
-        for (int g = 0; g < c.r.G; ++g)
-            order[g] = g;
-        auto gtiles = [&](int g) { return (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM; };
-        if (together) {
-            std::stable_sort(order, order + c.r.G, [&](int p, int q) { return gtiles(p) > gtiles(q); });
-            for (int i = 0; i < c.r.G; ++i) {
-                int best = 0;
-                for (int x = 1; x < kXcds; ++x)
-                    if (cnt[x] < cnt[best])
-                        best = x;
-                xcd_of[order[i]] = best;
-                cnt[best] += gtiles(order[i]);
-            }
-            rows = *std::max_element(cnt, cnt + kXcds);
-        }
-        hostt = rows * kXcds <= kFusedHostTiles;
-        if (hostt) {
-            for (int i = 0; i < kFusedHostTiles; ++i)
-                a.tt[i] = TileEntry{0, 0, 0, 0};
-            int fill[kXcds] = {}, n = 0;
-            for (int g = 0; g < c.r.G; ++g) {
-                const int gs = c.r.k_offs[g], len = c.r.k_offs[g + 1] - gs;
-                const int gnt = gtiles(g);
-                for (int j = 0; j < gnt; ++j) {
-                    const int t0 = gs + (int)(((int64_t)len * j) / gnt);
-                    const int t1 = gs + (int)(((int64_t)len * (j + 1)) / gnt);
-                    const int pos = together ? fill[xcd_of[g]]++ * kXcds + xcd_of[g] : n++;
-                    a.tt[pos] = TileEntry{t0, t1 - t0, c.r.k_ids[g], len};
-                }
-            }
-        } else {
-            rows = (tiles + kXcds - 1) / kXcds;
-        }
-    }
+    bool hostt = c.r.kr && a.nf <= kFusedHostFt && fused_tile_table(c, a, rows);
+    if (!hostt)
+        rows = (tiles + kXcds - 1) / kXcds;
     // Every workgroup reads its token tile's x rows and its slice's A rows
     // whatever its feature tile, and that read is most of its time; halving
     // the feature tile doubles the workgroups without changing that read.
@@ -1991,6 +2029,87 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     }
 #undef LORA_FUSED
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
+// Short groups whose one-kernel delta would be slow: a K longer than 4096,
+// since each of that launch's workgroups reads its tile's x rows and its
+// slice's A rows over all of K (Llama-3-8B MLP down, K 14336: 20.9 -> 16.2 us
+// on the decode batch; the wide gate_up output, 24.4 -> 24.9 us, and the
+// attention families, 8.2 -> 14.4 us, stay on the one-kernel path).
+// LORA_SGMV_SPLITK_SHORT=0/1 forces the choice.
+bool splitk_short_wanted(const Common& c)
+{
+    const int e = env_int("LORA_SGMV_SPLITK_SHORT", -1);
+    if (e >= 0)
+        return e > 0;
+    return c.fs.in_f > 4096;
+}
+
+// The split-K delta for short groups: the one-kernel delta's shrink half with
+// K split over workgroups (fp32 slabs in the workspace, one load round trip
+// per workgroup), then the expand kernel, which adds the slabs in split order.
+// Returns LORA_ERR_UNSPECIFIED, before any launch, when it does not apply
+// (no host routing, too many tiles or splits for the launch tables, or too
+// small a workspace); the caller then takes the one-kernel path.
+lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, const void* A_stack,
+                               const void* B_stack, const void* bias, void* y, int64_t ldy, void* workspace,
+                               size_t workspace_bytes, int32_t path, hipStream_t s)
+{
+    if (!c.r.kr)
+        return LORA_ERR_UNSPECIFIED;
+    const int64_t tiles = fused_host_tiles(c);
+    if (tiles == 0)
+        return LORA_OK;
+    // splits: about one workgroup per compute unit, each wave at least one
+    // 32-element step and at most kXLdsSteps (x through LDS)
+    constexpr int kWaveK = kFusedWaves * 32;  // K of one step of every wave
+    const int units = (c.fs.in_f + kWaveK - 1) / kWaveK;
+    int S = (int)std::max<int64_t>(1, (device_cus() + tiles * c.fs.n_s / 2) / (tiles * c.fs.n_s));
+    S = std::min(std::max(S, (units + kXLdsSteps - 1) / kXLdsSteps), units);
+    while (S > 1 && c.fs.n_s * S > kFusedHostFt)
+        --S;
+    const int per = (units + S - 1) / S;  // steps per wave
+    if (per > kXLdsSteps)
+        return LORA_ERR_UNSPECIFIED;
+    S = (units + per - 1) / per;
+    const int64_t slab = (int64_t)c.r.end * c.fs.C;
+    if (!workspace || workspace_bytes < (size_t)S * slab * sizeof(float))
+        return LORA_ERR_UNSPECIFIED;
+    FusedArgs a;
+    fused_common_args(c, a, x, ldx, A_stack, B_stack, bias, y, ldy);
+    int64_t rows = 0;
+    if (!fused_tile_table(c, a, rows))
+        return LORA_ERR_UNSPECIFIED;
+    a.F = 0;  // no feature tiles: nothing of y or B is touched
+    for (int sl = 0; sl < 4; ++sl)
+        a.nft[sl] = 0;
+    a.nf = c.fs.n_s * S;
+    a.wave_steps = per;
+    a.kc = per * kWaveK;
+    a.slabs = reinterpret_cast<float*>(workspace);
+    a.slab = slab;
+    int ft = 0;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        for (int sp = 0; sp < S; ++sp)
+            a.fts[ft++] = make_int2(sl, sp);
+    for (; ft < kFusedHostFt; ++ft)
+        a.fts[ft] = make_int2(0, 0);
+    const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
+    const bool gather = c.r.rows != nullptr;
+    if (c.fs.R == 16) {
+        if (gather)
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, true, true>), g, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, false, true>), g, blk, 0, s, a);
+    } else {
+        if (gather)
+            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, true, true>), g, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, false, true>), g, blk, 0, s, a);
+    }
+    if (hipGetLastError() != hipSuccess)
+        return LORA_ERR_DEVICE;
+    return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
 }
 
 bool row_ok(int64_t ld, int64_t width, int elem)
@@ -2087,6 +2206,11 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
     if (workspace_bytes < delta_workspace(plan))
         return LORA_ERR_CAPACITY;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (path == LORA_PATH_AUTO && fused_auto(c) && splitk_short_wanted(c)) {
+        st = run_splitk_short(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, workspace, workspace_bytes, path, s);
+        if (st != LORA_ERR_UNSPECIFIED)
+            return st;
+    }
     if (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c)))
         return run_fused(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
     float* slabs = reinterpret_cast<float*>(workspace);
