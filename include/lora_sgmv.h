@@ -82,9 +82,10 @@ enum { LORA_TARGET_Q = 1, LORA_TARGET_K = 2, LORA_TARGET_V = 4, LORA_TARGET_O = 
 /* Kernel path selection for the device calls.  AUTO picks per token tile:
  * wavefront-reduction VALU code for short (decode-shaped) tiles, MFMA for
  * longer bf16 tiles; for lora_sgmv_delta, when the host copy of the routing
- * shows only short groups, the one-kernel path below, or for an input width
- * above 4096 its shrink half with K split over workgroups (partial sums in
- * the workspace) followed by the expand.  VALU / MFMA force one
+ * shows only short groups, the one-kernel path below, or, for an input width
+ * above 4096 or an output wide enough for more than two of its workgroups per
+ * compute unit, its shrink half with K split over workgroups (partial sums in
+ * the workspace) followed by its expand half.  VALU / MFMA force one
  * path (MFMA needs bf16; for the expand also a rank that is a multiple of 16
  * and at most 64 and slice widths that are multiples of 32).  FUSED (only
  * lora_sgmv_delta) forces the one-kernel path: shrink and expand of tiles of
@@ -371,8 +372,8 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  * lora_sgmv_expand (bias_stack as there); workspace >= lora_sgmv_workspace_bytes(dims, family, end)
  * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
  * path: any LORA_PATH_*; with the one-kernel path (FUSED, or AUTO on short
- * groups with an input width of at most 4096) the workspace is not touched
- * and y must not alias x or the stacks.
+ * groups when the split-K form above is not taken) the workspace is not
+ * touched and y must not alias x or the stacks.
  */
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
                               const void* A_stack, const void* B_stack, const void* bias_stack,

@@ -1316,9 +1316,10 @@ struct FusedArgs {
     int nft[4];      // feature tiles per slice
     int nf;          // feature tiles per token tile
     int krot;        // nonzero: wave w takes K range (w + feature tile) mod waves
-    int kc;          // SHRINK: K range of one split (a multiple of 32)
-    float* slabs;    // SHRINK: fp32 slab s at slabs + s * slab, each [end][C]
+    int kc;          // kPartShrink: K range of one split (a multiple of 32)
+    float* slabs;    // split launches: fp32 slab s at slabs + s * slab, each [end][C]
     int64_t slab;
+    int nsplit;      // kPartExpand: slabs to add (at most kFusedWaves)
     RouteArgs r;
     TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
     int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT);
@@ -1339,14 +1340,20 @@ constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x
 
 // HOSTT: the tile comes from the host-built table tt (entries with n = 0
 // pad the grid), else from locate_tile over the routing.
-// SHRINK: the shrink half alone, with K split over workgroups.  Workgroup
-// (tile, slice, split s) sums x . A over K range [s kc, (s + 1) kc) of its
-// slice and writes the tile's rows of slab s; the expand kernel adds the
-// slabs in split order.  Nothing of y or B is read.
-template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER, bool SHRINK = false>
+// PART kPartShrink: the shrink half alone, with K split over workgroups.
+// Workgroup (tile, slice, split s) sums x . A over K range [s kc, (s + 1) kc)
+// of its slice and writes the tile's rows of slab s.  Nothing of y or B is
+// read.
+// PART kPartExpand: the expand half alone, from those slabs: the tile's rows
+// of its slice's columns of every slab are loaded with y and B in one round
+// and added in LDS in split order (at most kFusedWaves slabs), in place of
+// the shrink.  Nothing of x or A is read.
+enum { kPartAll = 0, kPartShrink = 1, kPartExpand = 2 };
+template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER, int PART = kPartAll>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
-    static_assert(!SHRINK || HOSTT, "the shrink-only launch uses the host tile table");
+    constexpr bool SHRINK = PART == kPartShrink;
+    static_assert(PART == kPartAll || HOSTT, "the split launches use the host tile table");
     constexpr int R = 16 * NH;
     constexpr int kPartBytes = kFusedWaves * kFusedTileM * R * 4;
     constexpr int kXBytes = XLDS ? kFusedWaves * kXLdsWaveBytes : 0;
@@ -1441,80 +1448,97 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb)
         acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (XLDS) {
-        // x: eight LDS-DMA loads of 2 rows x 512 bytes into the wave's region
-        char* xw = smem + w * kXLdsWaveBytes;
-        {
-            const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
-            const Buf xv = rm.buf(a.x, a.ldx);
-#pragma unroll
+    if constexpr (PART != kPartExpand) {
+        if constexpr (XLDS) {
+            // x: eight LDS-DMA loads of 2 rows x 512 bytes into the wave's region
+            char* xw = smem + w * kXLdsWaveBytes;
+            {
+                const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
+                const Buf xv = rm.buf(a.x, a.ldx);
+    #pragma unroll
+                for (int i = 0; i < kXLdsSteps; ++i) {
+                    const int row = 2 * i + h;
+                    const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
+                    const int kk = kw0 + 8 * c;
+                    const int rr = min(row, ti.n - 1);
+                    const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
+                        (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
+                }
+            }
+            uint4 ar[kXLdsSteps][NH];
+    #pragma unroll
             for (int i = 0; i < kXLdsSteps; ++i) {
-                const int row = 2 * i + h;
-                const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
-                const int kk = kw0 + 8 * c;
-                const int rr = min(row, ti.n - 1);
-                const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
-                    (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
-            }
-        }
-        uint4 ar[kXLdsSteps][NH];
-#pragma unroll
-        for (int i = 0; i < kXLdsSteps; ++i) {
-            const int kk = kw0 + 32 * i + 8 * q;
-            const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
-#pragma unroll
-            for (int nb = 0; nb < NH; ++nb)
-                ar[i][nb] = ab.ld16(kk < kw1 ? nb * ablk + ao : kOOB);
-        }
-        // every load (y, B, x, A) is out before the first wait: one round trip
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < kXLdsSteps; ++i) {
-            // piece 4 i + q of row l16: load l16 / 2, half l16 % 2, rotated slot
-            const int c = 4 * i + q;
-            const int slot = 32 * (l16 & 1) + 8 * (c >> 3) + ((c + l16) & 7);
-            const uint4 xr = *reinterpret_cast<const uint4*>(xw + 1024 * (l16 >> 1) + 16 * slot);
-#pragma unroll
-            for (int nb = 0; nb < NH; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr),
-                                                                  __builtin_bit_cast(bf16x8_t, ar[i][nb]),
-                                                                  acc[nb], 0, 0, 0);
-        }
-        __syncthreads();  // every wave is done with its x region before part overwrites it
-    } else {
-        const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
-        for (int bt = 0; bt < nbatch; ++bt) {
-            uint4 xr[STEPS], ar[STEPS][NH];
-#pragma unroll
-            for (int i = 0; i < STEPS; ++i) {
-                const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
-                const bool ok = kk < kw1;
-                xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
-                // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
+                const int kk = kw0 + 32 * i + 8 * q;
                 const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
-#pragma unroll
+    #pragma unroll
                 for (int nb = 0; nb < NH; ++nb)
-                    ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+                    ar[i][nb] = ab.ld16(kk < kw1 ? nb * ablk + ao : kOOB);
             }
-            // keep every load of the batch ahead of the first MFMA: one round trip
+            // every load (y, B, x, A) is out before the first wait: one round trip
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < STEPS; ++i)
-#pragma unroll
+    #pragma unroll
+            for (int i = 0; i < kXLdsSteps; ++i) {
+                // piece 4 i + q of row l16: load l16 / 2, half l16 % 2, rotated slot
+                const int c = 4 * i + q;
+                const int slot = 32 * (l16 & 1) + 8 * (c >> 3) + ((c + l16) & 7);
+                const uint4 xr = *reinterpret_cast<const uint4*>(xw + 1024 * (l16 >> 1) + 16 * slot);
+    #pragma unroll
                 for (int nb = 0; nb < NH; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr),
                                                                       __builtin_bit_cast(bf16x8_t, ar[i][nb]),
                                                                       acc[nb], 0, 0, 0);
+            }
+            __syncthreads();  // every wave is done with its x region before part overwrites it
+        } else {
+            const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
+            for (int bt = 0; bt < nbatch; ++bt) {
+                uint4 xr[STEPS], ar[STEPS][NH];
+    #pragma unroll
+                for (int i = 0; i < STEPS; ++i) {
+                    const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
+                    const bool ok = kk < kw1;
+                    xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
+                    // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
+                    const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
+    #pragma unroll
+                    for (int nb = 0; nb < NH; ++nb)
+                        ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+                }
+                // keep every load of the batch ahead of the first MFMA: one round trip
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int i = 0; i < STEPS; ++i)
+    #pragma unroll
+                    for (int nb = 0; nb < NH; ++nb)
+                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
+                                                                          __builtin_bit_cast(bf16x8_t, ar[i][nb]),
+                                                                          acc[nb], 0, 0, 0);
+            }
+        }
+        // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
+    #pragma unroll
+        for (int nb = 0; nb < NH; ++nb)
+    #pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[(kr * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
+    } else {
+        // u of the tile from the slabs: entry e is 4 floats of slab e / Q,
+        // token row (e % Q) / (R / 4), columns 4 ((e % Q) % (R / 4)) .. + 3 of
+        // the slice; slabs past nsplit and rows past the tile read zero.
+        // Stored at wave index = slab, so the sum below adds the slabs in
+        // split order.
+        constexpr int Q = kFusedTileM * R / 4;
+        const Buf sb(a.slabs, (uint32_t)((size_t)a.nsplit * a.slab * 4));
+        for (int e = threadIdx.x; e < kFusedWaves * Q; e += kFusedThreads) {
+            const int sp = e / Q, rem = e % Q, t = rem / (R / 4), j4 = rem % (R / 4);
+            const bool ok = live && sp < a.nsplit && t < ti.n;
+            const uint4 v = sb.ld16(ok ? (uint32_t)(((size_t)sp * a.slab + (size_t)(ti.t0 + t) * a.C + sl * R + 4 * j4) * 4)
+                                       : kOOB);
+            *reinterpret_cast<uint4*>(part + (sp * kFusedTileM + t) * R + 4 * j4) = v;
         }
     }
-    // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
-#pragma unroll
-    for (int nb = 0; nb < NH; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            part[(kr * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
     __syncthreads();
     for (int e = threadIdx.x; e < kFusedTileM * R; e += kFusedThreads) {
         float v = part[e];
@@ -1863,6 +1887,62 @@ bool fused_auto(const Common& c)
 // 3.6 K tokens, -5 %; a 0.8 K-token mixed batch, +3 %).
 constexpr int kDeltaFoldTokens = 2048;
 
+// Feature tiles of width f: F, nft and nf of the launch arguments.
+void set_fused_feat(const Common& c, FusedArgs& a, int f)
+{
+    a.F = f;
+    a.nf = 0;
+    for (int sl = 0; sl < 4; ++sl) {
+        a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / f : 0;
+        a.nf += a.nft[sl];
+    }
+}
+
+// The widest feature tile: the largest power of two <= kFusedMaxFeat
+// dividing every slice width (LORA_SGMV_FUSED_FEAT caps it, for tuning).
+int fused_widest_feat(const Common& c)
+{
+    const int feat_env = env_int("LORA_SGMV_FUSED_FEAT", 0);
+    int F = feat_env > 0 ? std::min(std::max(feat_env, 32), kFusedMaxFeat) : kFusedMaxFeat;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        while (c.fs.widths[sl] % F)
+            F >>= 1;
+    return F;
+}
+
+// Final feature tiles once the grid height (rows, tiles per XCD) is known,
+// and the feature-tile table of a host-table launch.
+// Every workgroup of the one-kernel delta reads its token tile's x rows and
+// its slice's A rows whatever its feature tile, and that read is most of its
+// time; halving the feature tile doubles the workgroups without changing that
+// read.  So the tile is halved (down to 128 features) only while each XCD
+// still runs at most one workgroup per compute unit: then the extra
+// workgroups land on idle units and each one's y and B share shrinks.
+void fused_feature_tiles(const Common& c, FusedArgs& a, int64_t rows, bool hostt)
+{
+    int F = a.F;
+    if (env_int("LORA_SGMV_FUSED_FEAT", 0) <= 0) {
+        const int per_xcd = device_cus() / kXcds;
+        while (F > 128) {
+            int nf2 = 0;
+            for (int sl = 0; sl < c.fs.n_s; ++sl)
+                nf2 += c.fs.widths[sl] / (F / 2);
+            if (rows * nf2 > per_xcd || (hostt && nf2 > kFusedHostFt))
+                break;
+            F /= 2;
+        }
+        set_fused_feat(c, a, F);
+    }
+    if (hostt) {
+        int ft = 0;
+        for (int sl = 0; sl < c.fs.n_s; ++sl)
+            for (int i = 0; i < a.nft[sl]; ++i)
+                a.fts[ft++] = make_int2(sl, a.soff[sl] + i * a.F);
+        for (; ft < kFusedHostFt; ++ft)
+            a.fts[ft] = make_int2(0, 0);
+    }
+}
+
 // The launch arguments every one-kernel launch shares.
 void fused_common_args(const Common& c, FusedArgs& a, const void* x, int64_t ldx, const void* A_stack,
                        const void* B_stack, const void* bias, void* y, int64_t ldy)
@@ -1885,6 +1965,7 @@ void fused_common_args(const Common& c, FusedArgs& a, const void* x, int64_t ldx
     a.kc = 0;
     a.slabs = nullptr;
     a.slab = 0;
+    a.nsplit = 0;
     a.r = c.r;
 }
 
@@ -1946,22 +2027,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
 {
     FusedArgs a;
     fused_common_args(c, a, x, ldx, A_stack, B_stack, bias, y, ldy);
-    // feature tile: the largest power of two <= kFusedMaxFeat dividing every
-    // slice width (narrowed below once the tile count is known)
-    const int feat_env = env_int("LORA_SGMV_FUSED_FEAT", 0);
-    int F = feat_env > 0 ? std::min(std::max(feat_env, 32), kFusedMaxFeat) : kFusedMaxFeat;
-    for (int sl = 0; sl < c.fs.n_s; ++sl)
-        while (c.fs.widths[sl] % F)
-            F >>= 1;
-    auto set_feat = [&](int f) {
-        a.F = f;
-        a.nf = 0;
-        for (int sl = 0; sl < 4; ++sl) {
-            a.nft[sl] = sl < c.fs.n_s ? c.fs.widths[sl] / f : 0;
-            a.nf += a.nft[sl];
-        }
-    };
-    set_feat(F);
+    set_fused_feat(c, a, fused_widest_feat(c));
     const int steps = (c.fs.in_f + 31) / 32;
     a.wave_steps = (steps + kFusedWaves - 1) / kFusedWaves;
     // token tiles: exact count from the host routing, else a bound
@@ -1975,32 +2041,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     bool hostt = c.r.kr && a.nf <= kFusedHostFt && fused_tile_table(c, a, rows);
     if (!hostt)
         rows = (tiles + kXcds - 1) / kXcds;
-    // Every workgroup reads its token tile's x rows and its slice's A rows
-    // whatever its feature tile, and that read is most of its time; halving
-    // the feature tile doubles the workgroups without changing that read.
-    // So the tile is halved (down to 128 features) only while each XCD still
-    // runs at most one workgroup per compute unit: then the extra
-    // workgroups land on idle units and each one's y and B share shrinks.
-    if (feat_env <= 0) {
-        const int per_xcd = device_cus() / kXcds;
-        while (F > 128) {
-            int nf2 = 0;
-            for (int sl = 0; sl < c.fs.n_s; ++sl)
-                nf2 += c.fs.widths[sl] / (F / 2);
-            if (rows * nf2 > per_xcd || (hostt && nf2 > kFusedHostFt))
-                break;
-            F /= 2;
-        }
-        set_feat(F);
-    }
-    if (hostt) {
-        int ft = 0;
-        for (int sl = 0; sl < c.fs.n_s; ++sl)
-            for (int i = 0; i < a.nft[sl]; ++i)
-                a.fts[ft++] = make_int2(sl, a.soff[sl] + i * a.F);
-        for (; ft < kFusedHostFt; ++ft)
-            a.fts[ft] = make_int2(0, 0);
-    }
+    fused_feature_tiles(c, a, rows, hostt);
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
     const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
     const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
@@ -2031,23 +2072,31 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
-// Short groups whose one-kernel delta would be slow: a K longer than 4096,
-// since each of that launch's workgroups reads its tile's x rows and its
-// slice's A rows over all of K (Llama-3-8B MLP down, K 14336: 20.9 -> 16.2 us
-// on the decode batch; the wide gate_up output, 24.4 -> 24.9 us, and the
-// attention families, 8.2 -> 14.4 us, stay on the one-kernel path).
+// Short groups whose one-kernel delta would be slow: a K longer than 4096
+// (each of that launch's workgroups reads its tile's x rows and its slice's
+// A rows over all of K), or more than two of its workgroups per compute unit
+// at the widest feature tile (a wide output: every feature tile recomputes
+// the rank-space values).  On the Llama-3-8B decode batch: MLP down (K 14336)
+// 20.9 -> 10.2 us, gate_up (28 672 outputs) 24.6 -> 16.9 us; the attention
+// families stay on the one-kernel path (QKV 8.2 there, 10.3 us split).
 // LORA_SGMV_SPLITK_SHORT=0/1 forces the choice.
 bool splitk_short_wanted(const Common& c)
 {
     const int e = env_int("LORA_SGMV_SPLITK_SHORT", -1);
     if (e >= 0)
         return e > 0;
-    return c.fs.in_f > 4096;
+    if (c.fs.in_f > 4096)
+        return true;
+    int nf = 0;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        nf += c.fs.widths[sl] / fused_widest_feat(c);
+    return fused_host_tiles(c) * nf > 2 * (int64_t)device_cus();
 }
 
 // The split-K delta for short groups: the one-kernel delta's shrink half with
 // K split over workgroups (fp32 slabs in the workspace, one load round trip
-// per workgroup), then the expand kernel, which adds the slabs in split order.
+// per workgroup), then its expand half, which loads every slab of its tile
+// with y and B in one round and adds them in split order.
 // Returns LORA_ERR_UNSPECIFIED, before any launch, when it does not apply
 // (no host routing, too many tiles or splits for the launch tables, or too
 // small a workspace); the caller then takes the one-kernel path.
@@ -2065,7 +2114,7 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
     constexpr int kWaveK = kFusedWaves * 32;  // K of one step of every wave
     const int units = (c.fs.in_f + kWaveK - 1) / kWaveK;
     int S = (int)std::max<int64_t>(1, (device_cus() + tiles * c.fs.n_s / 2) / (tiles * c.fs.n_s));
-    S = std::min(std::max(S, (units + kXLdsSteps - 1) / kXLdsSteps), units);
+    S = std::min(std::max(S, (units + kXLdsSteps - 1) / kXLdsSteps), std::min(units, kFusedWaves));
     while (S > 1 && c.fs.n_s * S > kFusedHostFt)
         --S;
     const int per = (units + S - 1) / S;  // steps per wave
@@ -2098,18 +2147,38 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
     const bool gather = c.r.rows != nullptr;
     if (c.fs.R == 16) {
         if (gather)
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, true, true>), g, blk, 0, s, a);
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, true, kPartShrink>), g, blk, 0, s, a);
         else
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, false, true>), g, blk, 0, s, a);
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, true, true, false, kPartShrink>), g, blk, 0, s, a);
     } else {
         if (gather)
-            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, true, true>), g, blk, 0, s, a);
+            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, true, kPartShrink>), g, blk, 0, s, a);
         else
-            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, false, true>), g, blk, 0, s, a);
+            hipLaunchKernelGGL((fused_delta_kernel<2, 8, true, true, false, kPartShrink>), g, blk, 0, s, a);
     }
     if (hipGetLastError() != hipSuccess)
         return LORA_ERR_DEVICE;
-    return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
+    // the expand half: the same tiles, feature tiles as the one-kernel delta
+    FusedArgs b = a;
+    set_fused_feat(c, b, fused_widest_feat(c));
+    if (b.nf > kFusedHostFt)
+        return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
+    fused_feature_tiles(c, b, rows, true);
+    b.kc = 0;
+    b.nsplit = S;
+    const dim3 ge((unsigned)(kXcds * b.nf), (unsigned)rows);
+    if (c.fs.R == 16) {
+        if (gather)
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false, true, true, kPartExpand>), ge, blk, 0, s, b);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false, true, false, kPartExpand>), ge, blk, 0, s, b);
+    } else {
+        if (gather)
+            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false, true, true, kPartExpand>), ge, blk, 0, s, b);
+        else
+            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false, true, false, kPartExpand>), ge, blk, 0, s, b);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
 bool row_ok(int64_t ld, int64_t width, int elem)
