@@ -1309,7 +1309,8 @@ struct FusedArgs {
     uint16_t* y;
     int64_t ldy;
     int in_f, out_f;
-    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat)
+    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat; twice that
+                     // in the expand-only launch)
     int wave_steps;  // 32-element K steps per wave
     int C, n_s;
     int soff[5];
@@ -1344,11 +1345,120 @@ constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x
 // Workgroup (tile, slice, split s) sums x . A over K range [s kc, (s + 1) kc)
 // of its slice and writes the tile's rows of slab s.  Nothing of y or B is
 // read.
-// PART kPartExpand: the expand half alone, from those slabs: the tile's rows
-// of its slice's columns of every slab are loaded with y and B in one round
-// and added in LDS in split order (at most kFusedWaves slabs), in place of
-// the shrink.  Nothing of x or A is read.
+// PART kPartExpand: the expand half alone, from those slabs
+// (fused_expand_from_slabs).
 enum { kPartAll = 0, kPartShrink = 1, kPartExpand = 2 };
+
+// The expand half of the split-K delta, from the shrink half's slabs: one
+// workgroup per (16-token tile, feature tile of up to 1024 features), both
+// from the host tables.  Wave w expands the 32-feature pairs 32 w and
+// 32 w + 512 of the tile.  Its y runs, B rows and bias, and the tile's rows
+// of its slice's columns of every slab, are loaded in one round; the slabs
+// are added in LDS in split order (at most kFusedWaves of them) and the
+// result is expanded as in the one-kernel delta.  part: kFusedWaves * 16 * R
+// floats of LDS; us: 16 * R floats.
+template <int NH, bool GATHER>
+__device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, float* part, float* us)
+{
+    constexpr int R = 16 * NH;
+    constexpr int NPAIR = 2;
+    const int tile = blockIdx.y * kXcds + blockIdx.x % kXcds;
+    const int ftile = blockIdx.x / kXcds;
+    const TileEntry te = a.tt[min(tile, kFusedHostTiles - 1)];
+    const int2 fe = a.fts[min(ftile, kFusedHostFt - 1)];
+    const int sl = fe.x, f0 = fe.y;
+    const uint32_t live = te.n > 0 ? 1u : 0u;  // 0 for a padding tile
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int np = a.F >> 5;
+    const bool tok = l16 < te.n;
+    const RowMap<GATHER> rm{a.r.rows, te.t0, te.n, a.r.nrows};
+    const uint32_t trow = rm(l16);
+    const Buf yb = rm.buf(a.y, a.ldy);
+    const Buf biasb(a.bias + (size_t)te.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
+    const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);
+    uint32_t yoff[NPAIR];
+    uint4 yraw[NPAIR], braw_bias[NPAIR], bfr[NPAIR][2][NH];
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+        const int fp = 32 * (w + kFusedWaves * p);  // first feature of pair p in the tile
+        const bool pv = w + kFusedWaves * p < np;
+        yoff[p] = (pv && tok) ? (uint32_t)(trow * a.ldy + f0 + fp + 8 * q) * 2 : kOOB;
+        yraw[p] = yb.ld16(yoff[p]);
+        braw_bias[p] = biasb.ld16(pv ? (uint32_t)(fp + 8 * q) * 2 : kOOB);
+        // B rows as the M operand, permuted: row i of block h is feature
+        // fp + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kh = 0; kh < NH; ++kh)
+                bfr[p][h][kh] = bb.ld16(pv ? (uint32_t)((fp + mrow + 4 * h) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+    }
+    // u of the tile from the slabs: entry e is 4 floats of slab e / Q, token
+    // row (e % Q) / (R / 4), columns 4 ((e % Q) % (R / 4)) .. + 3 of the
+    // slice; slabs past nsplit and rows past the tile read zero
+    constexpr int Q = kFusedTileM * R / 4;
+    const Buf sb(a.slabs, (uint32_t)((size_t)a.nsplit * a.slab * 4));
+    for (int e = threadIdx.x; e < kFusedWaves * Q; e += kFusedThreads) {
+        const int sp = e / Q, rem = e % Q, t = rem / (R / 4), j4 = rem % (R / 4);
+        const bool ok = live && sp < a.nsplit && t < te.n;
+        const uint4 v = sb.ld16(ok ? (uint32_t)(((size_t)sp * a.slab + (size_t)(te.t0 + t) * a.C + sl * R + 4 * j4) * 4)
+                                   : kOOB);
+        *reinterpret_cast<uint4*>(part + (sp * kFusedTileM + t) * R + 4 * j4) = v;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kFusedTileM * R; e += kFusedThreads) {
+        float v = part[e];
+#pragma unroll
+        for (int sp = 1; sp < kFusedWaves; ++sp)
+            v += part[sp * kFusedTileM * R + e];
+        us[e] = v;
+    }
+    __syncthreads();
+    if (w >= np)
+        return;
+    // u = hi + lo in bf16 as the N operand (tokens), y as C
+    bf16x8_t uf[NH];
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) {
+        const float* up = us + l16 * R + 16 * kh + 8 * (q & 1);
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = up[2 * e], v1 = up[2 * e + 1];
+            uint32_t hi = f2bf_pair(v0, v1);
+            if (q >= 2)
+                hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+            pk[e] = hi;
+        }
+        uf[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+        if (w + kFusedWaves * p >= np)
+            break;
+        f32x4_t acc0 = {bf2f(yraw[p].x & 0xFFFFu), bf2f(yraw[p].x >> 16), bf2f(yraw[p].y & 0xFFFFu),
+                        bf2f(yraw[p].y >> 16)};
+        f32x4_t acc1 = {bf2f(yraw[p].z & 0xFFFFu), bf2f(yraw[p].z >> 16), bf2f(yraw[p].w & 0xFFFFu),
+                        bf2f(yraw[p].w >> 16)};
+        if (a.bias)
+            add_bias8(braw_bias[p], acc0, acc1);
+#pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[p][0][kh]), uf[kh],
+                                                          acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[p][1][kh]), uf[kh],
+                                                          acc1, 0, 0, 0);
+        }
+        uint4 o;
+        o.x = f2bf_pair(acc0[0], acc0[1]);
+        o.y = f2bf_pair(acc0[2], acc0[3]);
+        o.z = f2bf_pair(acc1[0], acc1[1]);
+        o.w = f2bf_pair(acc1[2], acc1[3]);
+        yb.st16(yoff[p], o);
+    }
+}
 template <int NH, int STEPS, bool XLDS, bool HOSTT, bool GATHER, int PART = kPartAll>
 __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 {
@@ -1363,6 +1473,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     __shared__ __attribute__((aligned(16))) char smem[(kXBytes > kPartBytes ? kXBytes : kPartBytes)];
     __shared__ float us[kFusedTileM * R];  // u of the tile
     float* part = reinterpret_cast<float*>(smem);
+    if constexpr (PART == kPartExpand) {
+        fused_expand_from_slabs<NH, GATHER>(a, part, us);
+        return;
+    }
 
     // grid (kXcds * nf, tiles / kXcds): the linear block id b = x + y * gridDim.x
     // runs over XCDs as b % kXcds, so the nf workgroups of tile y * kXcds +
@@ -1448,97 +1562,80 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
 #pragma unroll
     for (int nb = 0; nb < NH; ++nb)
         acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (PART != kPartExpand) {
-        if constexpr (XLDS) {
-            // x: eight LDS-DMA loads of 2 rows x 512 bytes into the wave's region
-            char* xw = smem + w * kXLdsWaveBytes;
-            {
-                const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
-                const Buf xv = rm.buf(a.x, a.ldx);
-    #pragma unroll
-                for (int i = 0; i < kXLdsSteps; ++i) {
-                    const int row = 2 * i + h;
-                    const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
-                    const int kk = kw0 + 8 * c;
-                    const int rr = min(row, ti.n - 1);
-                    const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
-                        (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
-                }
-            }
-            uint4 ar[kXLdsSteps][NH];
-    #pragma unroll
+    if constexpr (XLDS) {
+        // x: eight LDS-DMA loads of 2 rows x 512 bytes into the wave's region
+        char* xw = smem + w * kXLdsWaveBytes;
+        {
+            const int h = lane >> 5, u = (lane >> 3) & 3, j = lane & 7;
+            const Buf xv = rm.buf(a.x, a.ldx);
+#pragma unroll
             for (int i = 0; i < kXLdsSteps; ++i) {
-                const int kk = kw0 + 32 * i + 8 * q;
+                const int row = 2 * i + h;
+                const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
+                const int kk = kw0 + 8 * c;
+                const int rr = min(row, ti.n - 1);
+                const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
+                    (int)((rm(rr) * a.ldx + kc) * 2), 0, 0, 0);
+            }
+        }
+        uint4 ar[kXLdsSteps][NH];
+#pragma unroll
+        for (int i = 0; i < kXLdsSteps; ++i) {
+            const int kk = kw0 + 32 * i + 8 * q;
+            const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
+#pragma unroll
+            for (int nb = 0; nb < NH; ++nb)
+                ar[i][nb] = ab.ld16(kk < kw1 ? nb * ablk + ao : kOOB);
+        }
+        // every load (y, B, x, A) is out before the first wait: one round trip
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kXLdsSteps; ++i) {
+            // piece 4 i + q of row l16: load l16 / 2, half l16 % 2, rotated slot
+            const int c = 4 * i + q;
+            const int slot = 32 * (l16 & 1) + 8 * (c >> 3) + ((c + l16) & 7);
+            const uint4 xr = *reinterpret_cast<const uint4*>(xw + 1024 * (l16 >> 1) + 16 * slot);
+#pragma unroll
+            for (int nb = 0; nb < NH; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr),
+                                                                  __builtin_bit_cast(bf16x8_t, ar[i][nb]),
+                                                                  acc[nb], 0, 0, 0);
+        }
+        __syncthreads();  // every wave is done with its x region before part overwrites it
+    } else {
+        const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
+        for (int bt = 0; bt < nbatch; ++bt) {
+            uint4 xr[STEPS], ar[STEPS][NH];
+#pragma unroll
+            for (int i = 0; i < STEPS; ++i) {
+                const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
+                const bool ok = kk < kw1;
+                xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
+                // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
                 const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
-    #pragma unroll
+#pragma unroll
                 for (int nb = 0; nb < NH; ++nb)
-                    ar[i][nb] = ab.ld16(kk < kw1 ? nb * ablk + ao : kOOB);
+                    ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
             }
-            // every load (y, B, x, A) is out before the first wait: one round trip
+            // keep every load of the batch ahead of the first MFMA: one round trip
             __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int i = 0; i < kXLdsSteps; ++i) {
-                // piece 4 i + q of row l16: load l16 / 2, half l16 % 2, rotated slot
-                const int c = 4 * i + q;
-                const int slot = 32 * (l16 & 1) + 8 * (c >> 3) + ((c + l16) & 7);
-                const uint4 xr = *reinterpret_cast<const uint4*>(xw + 1024 * (l16 >> 1) + 16 * slot);
-    #pragma unroll
+#pragma unroll
+            for (int i = 0; i < STEPS; ++i)
+#pragma unroll
                 for (int nb = 0; nb < NH; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr),
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
                                                                       __builtin_bit_cast(bf16x8_t, ar[i][nb]),
                                                                       acc[nb], 0, 0, 0);
-            }
-            __syncthreads();  // every wave is done with its x region before part overwrites it
-        } else {
-            const int nbatch = (a.wave_steps + STEPS - 1) / STEPS;
-            for (int bt = 0; bt < nbatch; ++bt) {
-                uint4 xr[STEPS], ar[STEPS][NH];
-    #pragma unroll
-                for (int i = 0; i < STEPS; ++i) {
-                    const int kk = kw0 + 32 * (bt * STEPS + i) + 8 * q;
-                    const bool ok = kk < kw1;
-                    xr[i] = xb.ld16(ok ? xrow + (uint32_t)kk * 2 : kOOB);
-                    // piece kk / 8, row l16 of block nb: lane-contiguous 16-byte pieces
-                    const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 8) * 2;
-    #pragma unroll
-                    for (int nb = 0; nb < NH; ++nb)
-                        ar[i][nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
-                }
-                // keep every load of the batch ahead of the first MFMA: one round trip
-                __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                for (int i = 0; i < STEPS; ++i)
-    #pragma unroll
-                    for (int nb = 0; nb < NH; ++nb)
-                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i]),
-                                                                          __builtin_bit_cast(bf16x8_t, ar[i][nb]),
-                                                                          acc[nb], 0, 0, 0);
-            }
-        }
-        // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
-    #pragma unroll
-        for (int nb = 0; nb < NH; ++nb)
-    #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[(kr * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
-    } else {
-        // u of the tile from the slabs: entry e is 4 floats of slab e / Q,
-        // token row (e % Q) / (R / 4), columns 4 ((e % Q) % (R / 4)) .. + 3 of
-        // the slice; slabs past nsplit and rows past the tile read zero.
-        // Stored at wave index = slab, so the sum below adds the slabs in
-        // split order.
-        constexpr int Q = kFusedTileM * R / 4;
-        const Buf sb(a.slabs, (uint32_t)((size_t)a.nsplit * a.slab * 4));
-        for (int e = threadIdx.x; e < kFusedWaves * Q; e += kFusedThreads) {
-            const int sp = e / Q, rem = e % Q, t = rem / (R / 4), j4 = rem % (R / 4);
-            const bool ok = live && sp < a.nsplit && t < ti.n;
-            const uint4 v = sb.ld16(ok ? (uint32_t)(((size_t)sp * a.slab + (size_t)(ti.t0 + t) * a.C + sl * R + 4 * j4) * 4)
-                                       : kOOB);
-            *reinterpret_cast<uint4*>(part + (sp * kFusedTileM + t) * R + 4 * j4) = v;
         }
     }
+    // D: lane holds rank column 16 nb + lane % 16 of token rows 4 (lane / 16) + r
+#pragma unroll
+    for (int nb = 0; nb < NH; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            part[(kr * kFusedTileM + 4 * q + r) * R + 16 * nb + l16] = acc[nb][r];
     __syncthreads();
     for (int e = threadIdx.x; e < kFusedTileM * R; e += kFusedThreads) {
         float v = part[e];
@@ -2158,9 +2255,19 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
     }
     if (hipGetLastError() != hipSuccess)
         return LORA_ERR_DEVICE;
-    // the expand half: the same tiles, feature tiles as the one-kernel delta
+    // the expand half: the same tiles, feature tiles as the one-kernel delta;
+    // where 512-wide ones would put more than two workgroups on each compute
+    // unit, 1024-wide ones (two 32-feature pairs per wave), so that one
+    // round of workgroups covers more of the output
     FusedArgs b = a;
-    set_fused_feat(c, b, fused_widest_feat(c));
+    const int F = fused_widest_feat(c);
+    set_fused_feat(c, b, F);
+    bool wide = F == kFusedMaxFeat && rows * b.nf > 2 * (int64_t)(device_cus() / kXcds) &&
+                env_int("LORA_SGMV_EXPAND_PAIRS", 2) > 1;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        wide = wide && c.fs.widths[sl] % (2 * kFusedMaxFeat) == 0;
+    if (wide)
+        set_fused_feat(c, b, 2 * kFusedMaxFeat);
     if (b.nf > kFusedHostFt)
         return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
     fused_feature_tiles(c, b, rows, true);
