@@ -11,7 +11,14 @@ import synth
 import segmented_rank_gemv_amd as srg
 from lora_case import TOL, from_dev, log, rel_err, to_dev
 
+torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
 
 PATHS = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA, "fused": srg.PATH_FUSED}
 
@@ -122,4 +129,22 @@ def test_mlp_with_lora_bias(fam, fused, path):
         ranks = np.array([16, 8, 4, 12], np.int32)
     ey = run_family(w, fam, lengths, slots, ranks, path, fused, with_bias=True)
     log(f"[mlp-bias] family={fam} fused={fused} path={path} y_rel={ey:.3e}")
+    assert ey <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fam", [srg.FAMILY_GATE_UP, srg.FAMILY_DOWN])
+def test_split_k_short_wide_and_long(fam, monkeypatch):
+    """The split-K delta for short groups at shapes past its tables: an
+    intermediate width of 36 864 makes gate_up 73 728 features wide, more
+    than 64 feature tiles of 1024, so its expand half falls back to the
+    64-row expand kernel on the same slabs; down then has K = 36 864, split
+    into at most 16 K ranges of 8 steps per wave."""
+    base = synth.get_workload("mlp")
+    w = synth.Workload(**{**base.__dict__, "intermediate": 36864, "max_num_loras": 4})
+    # every group at most 32 tokens (slot 0: 1 + 30, slot 1: 24, slot 2: 16, slot 3: 0 + 3)
+    lengths = np.array([1, 24, 16, 0, 9, 30, 3], np.int64)
+    slots = np.array([0, 1, 2, 3, -1, 0, 3], np.int32)
+    monkeypatch.setenv("LORA_SGMV_SPLITK_SHORT", "1")
+    ey = run_family(w, fam, lengths, slots, np.full(w.max_num_loras, 16, np.int32), "auto", True)
+    log(f"[mlp] wide/long family={fam} y_rel={ey:.3e}")
     assert ey <= TOL["bf16"]
