@@ -1503,7 +1503,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
         // loads into two dependent rounds
         asm volatile("" ::"s"(a.x), "s"(a.A), "s"(a.B), "s"(a.y), "s"(a.ldx), "s"(a.ldy), "s"(a.a_slot),
                      "s"(a.in_f), "s"(a.out_f), "s"(a.F), "s"(a.wave_steps), "s"(te.t0), "s"(te.n), "s"(te.slot),
-                     "s"(fe.x), "s"(fe.y));
+                     "s"(te.glen), "s"(fe.x), "s"(fe.y), "s"(a.bias), "s"(a.krot));
     } else {
         if (!locate_tile<kFusedTileM, true>(a.r, tile, ti))
             return;
