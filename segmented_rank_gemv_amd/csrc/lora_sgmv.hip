@@ -262,6 +262,8 @@ struct RouteArgs {
     uint32_t nrows;   // rows of x and y under per-token routing
     int k_offs[LORA_MAX_HOST_GROUPS + 1];
     int k_ids[LORA_MAX_HOST_GROUPS];
+    // host copy: first kTileM-token tile of each group (k_tile0[G] = tiles)
+    int k_tile0[LORA_MAX_HOST_GROUPS + 1];
 };
 
 // Locate token tile `tile`: groups are cut into tiles of at most TM tokens
@@ -276,6 +278,26 @@ template <int TM, bool BAL>
 __device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
 {
     const int lane = threadIdx.x & 63;
+    if constexpr (TM == kTileM && !BAL) {
+        if (r.kr) {
+            // host copy: the groups' first tiles are in the arguments (at most
+            // 64 groups, one per lane), so one load and a ballot find the
+            // group; the host has checked the offsets (monotone, [0, end])
+            const int last = lane < r.G ? r.k_tile0[lane + 1] : 0;
+            const unsigned long long hit = __ballot(lane < r.G && tile < last);
+            if (!hit)
+                return false;
+            const int g = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+            const int gs = r.k_offs[g], ge = r.k_offs[g + 1];
+            const int t0 = gs + (tile - r.k_tile0[g]) * TM;
+            ti.g = g;
+            ti.t0 = t0;
+            ti.n = min(t0 + TM, ge) - t0;
+            ti.glen = ge - gs;
+            ti.slot = r.k_ids[g];
+            return ti.slot >= 0 && ti.slot < r.L;
+        }
+    }
     int base = 0;
     for (int c0 = 0; c0 < r.G; c0 += 64) {
         const int i = c0 + lane;
@@ -1839,6 +1861,9 @@ lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path
         }
         for (int g = 0; g <= G; ++g)
             r.k_offs[g] = o[g];
+        r.k_tile0[0] = 0;
+        for (int g = 0; g < G; ++g)
+            r.k_tile0[g + 1] = r.k_tile0[g] + (o[g + 1] - o[g] + kTileM - 1) / kTileM;
         r.kr = 1;
     }
     return LORA_OK;
