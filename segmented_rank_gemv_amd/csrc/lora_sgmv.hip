@@ -283,18 +283,25 @@ __device__ bool locate_tile(const RouteArgs& r, int tile, TileInfo& ti)
             // host copy: the groups' first tiles are in the arguments (at most
             // 64 groups, one per lane), so one load and a ballot find the
             // group; the host has checked the offsets (monotone, [0, end])
-            const int last = lane < r.G ? r.k_tile0[lane + 1] : 0;
-            const unsigned long long hit = __ballot(lane < r.G && tile < last);
+            // lane g loads group g's entries, all in one round; the group's
+            // values are then read from its lane, with no second round
+            const bool in = lane < r.G;
+            const int first_l = in ? r.k_tile0[lane] : 0;
+            const int last_l = in ? r.k_tile0[lane + 1] : 0;
+            const int gs_l = in ? r.k_offs[lane] : 0;
+            const int ge_l = in ? r.k_offs[lane + 1] : 0;
+            const int id_l = in ? r.k_ids[lane] : -1;
+            const unsigned long long hit = __ballot(in && tile < last_l);
             if (!hit)
                 return false;
             const int g = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
-            const int gs = r.k_offs[g], ge = r.k_offs[g + 1];
-            const int t0 = gs + (tile - r.k_tile0[g]) * TM;
+            const int gs = __builtin_amdgcn_readlane(gs_l, g), ge = __builtin_amdgcn_readlane(ge_l, g);
+            const int t0 = gs + (tile - __builtin_amdgcn_readlane(first_l, g)) * TM;
             ti.g = g;
             ti.t0 = t0;
             ti.n = min(t0 + TM, ge) - t0;
             ti.glen = ge - gs;
-            ti.slot = r.k_ids[g];
+            ti.slot = __builtin_amdgcn_readlane(id_l, g);
             return ti.slot >= 0 && ti.slot < r.L;
         }
     }
@@ -613,6 +620,11 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(ShrinkArgs a)
                                   ? (kHasMfma ? ShrinkLds<NB, KC>::kElems * 2 : 0)
                                   : (kHasValu ? kValuLds : 0);
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes > 0 ? kLdsBytes : 16];
+    // the arguments the data addresses need, in scalar registers before the
+    // tile lookup, so that they load in the same round as its own arguments
+    asm volatile("" ::"s"(a.x), "s"(a.ldx), "s"(a.A), "s"(a.a_slot), "s"(a.out), "s"(a.slab), "s"(a.in_f), "s"(a.C),
+                 "s"(a.S), "s"(a.kc), "s"(a.nz), "s"(a.cb), "s"(a.valu_max), "s"(a.r.G), "s"(a.r.end), "s"(a.r.L),
+                 "s"(a.r.kr));
 
     const int lin = blockIdx.x;
     const int z = lin % a.nz;
@@ -1252,6 +1264,11 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
     uint16_t* blds = ylds + kTileM * kYLd;
     // the bias row of the tile, after the y and B tiles (only with a bias)
     uint16_t* bls = ylds + (NH == 1 ? kTileM * kYLd + kExpandCols * 16 : NH == 2 || NH == 4 ? kExpandCols * 16 * NH : 0);
+    // the arguments the data addresses need, in scalar registers before the
+    // tile lookup, so that they load in the same round as its own arguments
+    asm volatile("" ::"s"(a.u), "s"(a.slab), "s"(a.S), "s"(a.B), "s"(a.y), "s"(a.ldy), "s"(a.C), "s"(a.R),
+                 "s"(a.out_f), "s"(a.ft), "s"(a.n_ftiles), "s"(a.valu_max), "s"(a.bias), "s"(a.r.G), "s"(a.r.end),
+                 "s"(a.r.L), "s"(a.r.kr));
 
     const int lin = blockIdx.x;
     const int ftile = lin % a.n_ftiles;
