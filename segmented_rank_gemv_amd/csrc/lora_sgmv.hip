@@ -1348,8 +1348,8 @@ struct FusedArgs {
     uint16_t* y;
     int64_t ldy;
     int in_f, out_f;
-    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat; twice that
-                     // in the expand-only launch)
+    int F;           // feature tile width (multiple of 32, at most kFusedMaxFeat; up to four
+                     // times that in the expand-only launch)
     int wave_steps;  // 32-element K steps per wave
     int C, n_s;
     int soff[5];
@@ -1386,21 +1386,20 @@ constexpr int kXLdsWaveBytes = 16 * 32 * kXLdsSteps * 2;  // 16 rows x 8 steps x
 // read.
 // PART kPartExpand: the expand half alone, from those slabs
 // (fused_expand_from_slabs).
-enum { kPartAll = 0, kPartShrink = 1, kPartExpand = 2 };
+enum { kPartAll = 0, kPartShrink = 1, kPartExpand = 2, kPartExpand4 = 3 };
 
 // The expand half of the split-K delta, from the shrink half's slabs: one
-// workgroup per (16-token tile, feature tile of up to 1024 features), both
-// from the host tables.  Wave w expands the 32-feature pairs 32 w and
-// 32 w + 512 of the tile.  Its y runs, B rows and bias, and the tile's rows
+// workgroup per (16-token tile, feature tile of up to 512 NPAIR features),
+// both from the host tables.  Wave w expands the 32-feature pairs 32 w + 512 p
+// of the tile, p < NPAIR.  Its y runs, B rows and bias, and the tile's rows
 // of its slice's columns of every slab, are loaded in one round; the slabs
 // are added in LDS in split order (at most kFusedWaves of them) and the
 // result is expanded as in the one-kernel delta.  part: kFusedWaves * 16 * R
 // floats of LDS; us: 16 * R floats.
-template <int NH, bool GATHER>
+template <int NH, bool GATHER, int NPAIR>
 __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, float* part, float* us)
 {
     constexpr int R = 16 * NH;
-    constexpr int NPAIR = 2;
     const int tile = blockIdx.y * kXcds + blockIdx.x % kXcds;
     const int ftile = blockIdx.x / kXcds;
     const TileEntry te = a.tt[min(tile, kFusedHostTiles - 1)];
@@ -1512,8 +1511,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     __shared__ __attribute__((aligned(16))) char smem[(kXBytes > kPartBytes ? kXBytes : kPartBytes)];
     __shared__ float us[kFusedTileM * R];  // u of the tile
     float* part = reinterpret_cast<float*>(smem);
-    if constexpr (PART == kPartExpand) {
-        fused_expand_from_slabs<NH, GATHER>(a, part, us);
+    if constexpr (PART == kPartExpand || PART == kPartExpand4) {
+        fused_expand_from_slabs<NH, GATHER, PART == kPartExpand4 ? 4 : 2>(a, part, us);
         return;
     }
 
@@ -2299,34 +2298,53 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
         return LORA_ERR_DEVICE;
     // the expand half: the same tiles, feature tiles as the one-kernel delta;
     // where 512-wide ones would put more than two workgroups on each compute
-    // unit, 1024-wide ones (two 32-feature pairs per wave), so that one
-    // round of workgroups covers more of the output
+    // unit, 1024- or 2048-wide ones (two or four 32-feature pairs per wave):
+    // the narrowest that puts at most one workgroup on each compute unit, so
+    // that one round of workgroups covers the output
     FusedArgs b = a;
     const int F = fused_widest_feat(c);
     set_fused_feat(c, b, F);
-    bool wide = F == kFusedMaxFeat && rows * b.nf > 2 * (int64_t)(device_cus() / kXcds) &&
-                env_int("LORA_SGMV_EXPAND_PAIRS", 2) > 1;
-    for (int sl = 0; sl < c.fs.n_s; ++sl)
-        wide = wide && c.fs.widths[sl] % (2 * kFusedMaxFeat) == 0;
-    if (wide)
-        set_fused_feat(c, b, 2 * kFusedMaxFeat);
+    const int64_t per_xcd = device_cus() / kXcds;
+    int pairs = 1;
+    if (F == kFusedMaxFeat && rows * b.nf > 2 * per_xcd) {
+        const int most = std::min(std::max(env_int("LORA_SGMV_EXPAND_PAIRS", 4), 1), 4);
+        for (int p = 2; p <= most; p *= 2) {
+            bool fits = true;
+            for (int sl = 0; sl < c.fs.n_s; ++sl)
+                fits = fits && c.fs.widths[sl] % (p * kFusedMaxFeat) == 0;
+            if (!fits)
+                break;
+            pairs = p;
+            set_fused_feat(c, b, p * kFusedMaxFeat);
+            if (rows * b.nf <= per_xcd)
+                break;
+        }
+    }
     if (b.nf > kFusedHostFt)
         return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
     fused_feature_tiles(c, b, rows, true);
     b.kc = 0;
     b.nsplit = S;
     const dim3 ge((unsigned)(kXcds * b.nf), (unsigned)rows);
+#define LORA_EXPAND_HALF(NH, ST, PT)                                                                \
+    if (gather)                                                                                     \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, false, true, true, PT>), ge, blk, 0, s, b); \
+    else                                                                                            \
+        hipLaunchKernelGGL((fused_delta_kernel<NH, ST, false, true, false, PT>), ge, blk, 0, s, b);
     if (c.fs.R == 16) {
-        if (gather)
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false, true, true, kPartExpand>), ge, blk, 0, s, b);
-        else
-            hipLaunchKernelGGL((fused_delta_kernel<1, 8, false, true, false, kPartExpand>), ge, blk, 0, s, b);
+        if (pairs == 4) {
+            LORA_EXPAND_HALF(1, 8, kPartExpand4)
+        } else {
+            LORA_EXPAND_HALF(1, 8, kPartExpand)
+        }
     } else {
-        if (gather)
-            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false, true, true, kPartExpand>), ge, blk, 0, s, b);
-        else
-            hipLaunchKernelGGL((fused_delta_kernel<2, 4, false, true, false, kPartExpand>), ge, blk, 0, s, b);
+        if (pairs == 4) {
+            LORA_EXPAND_HALF(2, 4, kPartExpand4)
+        } else {
+            LORA_EXPAND_HALF(2, 4, kPartExpand)
+        }
     }
+#undef LORA_EXPAND_HALF
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
