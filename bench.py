@@ -587,8 +587,14 @@ def main():
             t_cpu += time.perf_counter() - t0
             tokens_done += sum(len(rows[i]) for i in reqs)
             n_calls += 1
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+        except OSError:
+            pass
         cpu = {"value": tokens_done / t_cpu, "unit": "LoRA tokens x layers / s", "cores": 1,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model, "host_cpus_available": len(os.sched_getaffinity(0)),
                "sample": f"{tokens_done} LoRA-routed token rows through the {proj_desc} delta of one layer "
                          f"({n_calls} oracle passes over {len(prepared)} distinct layers of the same "
                          f"workload, at most {budget} rows per pass), fp64, single thread, {t_cpu:.1f} s"}
