@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 7
+#define LORA_ABI_VERSION 8
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -284,8 +284,9 @@ lora_status_t lora_sgmv_workspace_bytes(const lora_dims_t* dims, int32_t family,
  *                  entries must be distinct (two positions on one y row
  *                  race); an entry outside [0, num_rows) reads zeros and
  *                  writes nothing.  Requires end <= num_rows and
- *                  (num_rows + 1) * row stride * element size < 2^32 bytes
- *                  for x and y.  Rows not listed are neither read nor written.
+ *                  (num_rows + 1) * row stride * element size <= 2^31 bytes
+ *                  for x and y (else LORA_ERR_INVALID_ARGUMENT, before any
+ *                  launch).  Rows not listed are neither read nor written.
  * A base-only or empty batch (G = 0 or end = 0) makes every device call a
  * no-op (the base-only routing of [MAX-lora] 运行时工作流与调度交互 — all tokens
  * on slot 0 holding all-zero adapters — is also valid and leaves y as is).
@@ -357,6 +358,31 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
                                const void* B_stack, const void* bias_stack, const lora_routing_t* routing,
                                void* y, int64_t ldy, int32_t path, void* stream);
 
+/* Tuning choices of lora_sgmv_delta.  None changes what is computed, only
+ * which kernels compute it (and so the fp32 summation order); a NULL pointer
+ * means the library's defaults, which are the measured best.  A negative
+ * value (0 for fused_feature_tile) selects the default of that field.
+ *   fused_max_tokens    AUTO takes the one-kernel path when no group has more
+ *                       tokens than this (default 32; 0: never).
+ *   splitk_short        on that path, the split-K form for an input width
+ *                       above 4096 or a wide output: -1 automatic, 0 never,
+ *                       1 whenever it applies (needs the workspace).
+ *   fused_feature_tile  widest feature tile of the one-kernel path: 0
+ *                       automatic, else a power of two in [32, 512]
+ *                       (else LORA_ERR_INVALID_ARGUMENT).
+ *   fused_k_rotation    staggered K ranges of the one-kernel path's waves:
+ *                       -1 default (on), 0 off, 1 on.
+ *   fold_slabs          two-kernel path: add the shrink's K-split partial
+ *                       sums in a separate pass before the expand: -1 from
+ *                       2048 LoRA-routed tokens, 0 never, 1 always. */
+typedef struct lora_options {
+    int32_t fused_max_tokens;
+    int32_t splitk_short;
+    int32_t fused_feature_tile;
+    int32_t fused_k_rotation;
+    int32_t fold_slabs;
+} lora_options_t;
+
 /* ---------------------------------------------------------------------------
  * lora_sgmv_delta — device, asynchronous on `stream`.
  *
@@ -370,15 +396,19 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  * for t < end, fp32 accumulation, one rounding to dims->dtype.  Rows >= end
  * are neither read nor written.  Arguments as for lora_sgmv_shrink and
  * lora_sgmv_expand (bias_stack as there); workspace >= lora_sgmv_workspace_bytes(dims, family, end)
- * bytes, never NULL when end > 0; it must not alias x, y or the stacks.
+ * bytes, 16-byte aligned; it must not alias x, y or the stacks.
  * path: any LORA_PATH_*; with the one-kernel path (FUSED, or AUTO on short
  * groups when the split-K form above is not taken) the workspace is not
- * touched and y must not alias x or the stacks.
+ * touched and may be NULL (AUTO then never takes the split-K form), and y
+ * must not alias x or the stacks.  On the other paths a NULL workspace is
+ * LORA_ERR_INVALID_ARGUMENT and a short one LORA_ERR_CAPACITY.
+ * options: NULL or the tuning choices above.
  */
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
                               const void* A_stack, const void* B_stack, const void* bias_stack,
                               const lora_routing_t* routing, void* y, int64_t ldy, void* workspace,
-                              size_t workspace_bytes, int32_t path, void* stream);
+                              size_t workspace_bytes, int32_t path, const lora_options_t* options,
+                              void* stream);
 
 /* ---------------------------------------------------------------------------
  * Adapter slot cache — host, synchronous.

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     PATH_VALU,
     MAX_HOST_GROUPS,
     LoraDims,
+    LoraOptions,
     LoraRouting,
     LoraError,
     a_tiled_shape,

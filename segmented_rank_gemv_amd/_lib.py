@@ -51,6 +51,28 @@ class _LoraRouting(ctypes.Structure):
 MAX_HOST_GROUPS = 64
 
 
+class _LoraOptions(ctypes.Structure):
+    _fields_ = [("fused_max_tokens", ctypes.c_int32), ("splitk_short", ctypes.c_int32),
+                ("fused_feature_tile", ctypes.c_int32), ("fused_k_rotation", ctypes.c_int32),
+                ("fold_slabs", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class LoraOptions:
+    """Tuning choices of lora_sgmv_delta (lora_options_t).  -1 (0 for
+    fused_feature_tile) keeps the library default; none changes what is
+    computed, only which kernels compute it."""
+    fused_max_tokens: int = -1
+    splitk_short: int = -1
+    fused_feature_tile: int = 0
+    fused_k_rotation: int = -1
+    fold_slabs: int = -1
+
+    def c(self) -> _LoraOptions:
+        return _LoraOptions(self.fused_max_tokens, self.splitk_short, self.fused_feature_tile,
+                            self.fused_k_rotation, self.fold_slabs)
+
+
 class LoraRouting:
     """The routing triple of a batch for the device calls: lora_ids and
     grouped_offsets as int32 GPU tensors, `end` and the group count on the
@@ -127,9 +149,8 @@ class LoraDims:
 
 
 def library_path() -> str:
-    """The library this process loads: liblora_sgmv.so next to this file, or
-    the file LORA_SGMV_LIB names (an alternative build, for A/B tuning)."""
-    return os.environ.get("LORA_SGMV_LIB") or _LIB_PATH
+    """The library this process loads: liblora_sgmv.so next to this file."""
+    return _LIB_PATH
 
 
 _lib = None
@@ -167,7 +188,8 @@ def _load():
     lib.lora_sgmv_expand.restype = i32
     lib.lora_sgmv_expand.argtypes = [D, i32, P, P, P, RT, P, i64, i32, P]
     lib.lora_sgmv_delta.restype = i32
-    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, RT, P, i64, P, ctypes.c_size_t, i32, P]
+    lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, RT, P, i64, P, ctypes.c_size_t, i32,
+                                    ctypes.POINTER(_LoraOptions), P]
     lib.lora_pack_bias.restype = i32
     lib.lora_pack_bias.argtypes = [D, i32, u32, P, P]
     I32P, I64P = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -449,16 +471,20 @@ def lora_sgmv_expand(dims: LoraDims, family: int, u, B_stack, routing: LoraRouti
 
 
 def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, routing: LoraRouting, y,
-                    workspace, path: int = PATH_AUTO, stream=None, bias=None) -> None:
+                    workspace, path: int = PATH_AUTO, stream=None, bias=None,
+                    options: Optional[LoraOptions] = None) -> None:
     """y[:end] += per-segment B[slot] . (A[slot] . x) (+ bias[slot] when a
-    bias stack [L, out] is given), shrink and expand in one call."""
+    bias stack [L, out] is given), shrink and expand in one call.  workspace
+    may be None where the one-kernel path runs; options: LoraOptions or None
+    (the library defaults)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dc, rc = dims.c(), routing.c()
+    oc = None if options is None else ctypes.byref(options.c())
     _check(_load().lora_sgmv_delta(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
                                     _dev_ptr(A_stack, "A_stack"), _dev_ptr(B_stack, "B_stack"),
                                     _dev_ptr(bias, "bias"), ctypes.byref(rc), _dev_ptr(y, "y"),
                                     _row_stride(y, "y"),
-                                    _dev_ptr(workspace, "workspace"), ws_bytes, int(path),
+                                    _dev_ptr(workspace, "workspace"), ws_bytes, int(path), oc,
                                     _stream_handle(stream)),
            "lora_sgmv_delta")
 

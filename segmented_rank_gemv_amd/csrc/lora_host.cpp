@@ -84,13 +84,6 @@ lora_status_t family_shape(const lora_dims_t* d, int32_t family, FamilyShape* fs
     return LORA_OK;
 }
 
-static int shrink_target_blocks()
-{
-    const char* v = getenv("LORA_SGMV_SHRINK_BLOCKS");
-    const int t = v && *v ? atoi(v) : 0;
-    return t > 0 ? t : kShrinkTargetBlocks;
-}
-
 static ShrinkPlan plan_from_tiles(const FamilyShape& fs, int n_tiles, int64_t end)
 {
     ShrinkPlan p;
@@ -100,7 +93,7 @@ static ShrinkPlan plan_from_tiles(const FamilyShape& fs, int n_tiles, int64_t en
     p.cb = ((fs.C + p.nz - 1) / p.nz + 15) / 16 * 16;
     const int grains = (fs.in_f + kKGrain - 1) / kKGrain;
     const int blocks = std::max(1, n_tiles * p.nz);
-    const int target = shrink_target_blocks();
+    const int target = kShrinkTargetBlocks;
     int S = (target + blocks - 1) / blocks;
     S = std::min(std::max(S, 1), grains);
     p.kc = (grains + S - 1) / S * kKGrain;

@@ -20,8 +20,7 @@ constexpr int kKGrain = 128;
 // largest power of two <= this that divides every slice width, so that a
 // tile never straddles two slices.
 constexpr int kExpandCols = 256;
-// Workgroups a shrink launch aims for before it stops splitting K
-// (LORA_SGMV_SHRINK_BLOCKS overrides it for tuning).
+// Workgroups a shrink launch aims for before it stops splitting K.
 constexpr int kShrinkTargetBlocks = 512;
 // Largest rank the kernels accept (bounds the expand's LDS u tile to 32 KB).
 constexpr int kMaxRank = 128;

@@ -34,7 +34,6 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
-#include <stdlib.h>
 #include <string.h>
 
 #include "lora_internal.h"
@@ -71,7 +70,9 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 // Buffer-resource access (raw buffer loads/stores with a byte offset).  An
 // offset at or past the resource size reads as zero and drops stores, which
 // masks rows and K positions without branches; every resource covers less
-// than 2^31 bytes and every masked offset is kOOB plus a small constant.
+// than 2^31 bytes (the entry points check this for the per-token layout,
+// where one resource spans all of x or y) and every masked offset is kOOB
+// plus a small constant.
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Cache policy bits of an access (kKeep: default; kStream: non-temporal).
@@ -236,8 +237,9 @@ struct RowMap {
     uint32_t nrows;
     __device__ __forceinline__ uint32_t operator()(int r) const
     {
+        // a negative r (possible on a padding tile, n = 0) is past the tile too
         if constexpr (GATHER)
-            return r < n ? min((uint32_t)idx[t0 + r], nrows) : nrows;
+            return (uint32_t)r < (uint32_t)n ? min((uint32_t)idx[t0 + r], nrows) : nrows;
         else
             return (uint32_t)r;
     }
@@ -1611,7 +1613,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
                 const int row = 2 * i + h;
                 const int c = 8 * u + ((j - row) & 7);  // piece of the row this lane carries
                 const int kk = kw0 + 8 * c;
-                const int rr = min(row, ti.n - 1);
+                const int rr = max(min(row, ti.n - 1), 0);
                 const int kc = kk < kw1 ? kk : min(kw0, a.in_f - 8);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xv.r, (__attribute__((address_space(3))) void*)(xw + 1024 * i), 16,
@@ -1749,15 +1751,9 @@ int device_cus()
     return n;
 }
 
-// Default VALU/MFMA split (tokens per tile); overridable for tuning through
-// LORA_SGMV_VALU_MAX_SHRINK / LORA_SGMV_VALU_MAX_EXPAND.
-int env_int(const char* name, int dflt)
-{
-    const char* v = getenv(name);
-    if (!v || !*v)
-        return dflt;
-    return atoi(v);
-}
+// Groups of at most this many tokens take the VALU path on AUTO (rank 16;
+// ranks 32 and up take the MFMA path for every tile).
+constexpr int kValuMaxTokens = 8;
 
 int valu_max_for(int path, bool mfma_ok, int dflt_auto)
 {
@@ -1826,18 +1822,62 @@ int pick_mode(int path, bool mfma_ok, int valu_max, const RouteArgs& r)
     return kMixed;
 }
 
+// The caller's tuning choices (lora_options_t), resolved to values.
+struct Tuning {
+    int fused_max;     // longest group for which AUTO takes the one-kernel delta
+    int splitk_short;  // -1 auto, 0 never, 1 whenever it applies
+    int feat;          // one-kernel feature tile cap (0: automatic)
+    int krot;          // staggered wave K ranges in the one-kernel delta
+    int fold;          // -1 auto, 0 never, 1 always
+};
+
+// Longest group for which AUTO takes the one-kernel delta, and the LoRA
+// token count from which lora_sgmv_delta folds the shrink's slabs before the
+// expand (measured: Llama-3-8B prefill, 12.6 K tokens, -3 %; 3.6 K tokens,
+// -5 %; a 0.8 K-token mixed batch, +3 %).
+constexpr int kFusedMaxTokens = 32;
+constexpr int kDeltaFoldTokens = 2048;
+
+lora_status_t resolve_options(const lora_options_t* o, Tuning* t)
+{
+    t->fused_max = kFusedMaxTokens;
+    t->splitk_short = -1;
+    t->feat = 0;
+    t->krot = 1;
+    t->fold = -1;
+    if (!o)
+        return LORA_OK;
+    if (o->fused_max_tokens >= 0)
+        t->fused_max = o->fused_max_tokens;
+    t->splitk_short = o->splitk_short < 0 ? -1 : o->splitk_short > 0;
+    if (o->fused_feature_tile != 0) {
+        const int f = o->fused_feature_tile;
+        if (f < 32 || f > 512 || (f & (f - 1)) != 0)
+            return LORA_ERR_INVALID_ARGUMENT;
+        t->feat = f;
+    }
+    if (o->fused_k_rotation >= 0)
+        t->krot = o->fused_k_rotation > 0;
+    t->fold = o->fold_slabs < 0 ? -1 : o->fold_slabs > 0;
+    return LORA_OK;
+}
+
 struct Common {
     FamilyShape fs;
     bool bf16;
     RouteArgs r;
+    Tuning t;
 };
 
 // Checks dims, family, path and the routing; fills the kernels' routing
 // arguments (with the host copy of the routing when one is given).
 lora_status_t check_common(const lora_dims_t* dims, int32_t family, int32_t path,
-                           const lora_routing_t* rt, Common* c)
+                           const lora_routing_t* rt, const lora_options_t* opts, Common* c)
 {
     lora_status_t st = family_shape(dims, family, &c->fs);
+    if (st != LORA_OK)
+        return st;
+    st = resolve_options(opts, &c->t);
     if (st != LORA_OK)
         return st;
     if (path < LORA_PATH_AUTO || path > LORA_PATH_FUSED || !rt)
@@ -1915,7 +1955,7 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
     // ranks 32 and up take the MFMA path for every tile: the VALU path keeps
     // one chunk in flight and runs eight token rows per chunk whatever the
     // tile's length, which loses to the MFMA tile even for one-token groups
-    a.valu_max = valu_max_for(path, shrink_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_SHRINK", c.fs.R >= 32 ? 0 : 8));
+    a.valu_max = valu_max_for(path, shrink_mfma_ok(c), c.fs.R >= 32 ? 0 : kValuMaxTokens);
     a.r = c.r;
     const int64_t grid = (int64_t)plan.n_tiles * plan.S * plan.nz;
     if (grid > 2147483647LL)
@@ -1975,7 +2015,7 @@ lora_status_t run_expand(const Common& c, const float* u, int64_t slab, int S, c
     // ranks 32 and 64 take the MFMA path (B through LDS) for every tile: the
     // VALU path reads B rows strided and is L1-bound there
     const bool lds_b = c.fs.R == 32 || c.fs.R == 64;
-    a.valu_max = valu_max_for(path, expand_mfma_ok(c), env_int("LORA_SGMV_VALU_MAX_EXPAND", lds_b ? 0 : 8));
+    a.valu_max = valu_max_for(path, expand_mfma_ok(c), lds_b ? 0 : kValuMaxTokens);
     a.r = c.r;
     const int64_t tiles = ((int64_t)c.r.end + kTileM - 1) / kTileM + c.r.G;
     const int64_t grid = tiles * a.n_ftiles;
@@ -2008,22 +2048,16 @@ bool fused_ok(const Common& c)
 }
 
 // AUTO takes the one-kernel delta when the host copy of the routing shows
-// that no group is longer than LORA_SGMV_FUSED_MAX tokens (default 32).
+// that no group is longer than the fused_max_tokens option (default 32).
 bool fused_auto(const Common& c)
 {
     if (!fused_ok(c) || !c.r.kr)
         return false;
-    const int lim = env_int("LORA_SGMV_FUSED_MAX", 32);
     for (int g = 0; g < c.r.G; ++g)
-        if (c.r.k_offs[g + 1] - c.r.k_offs[g] > lim)
+        if (c.r.k_offs[g + 1] - c.r.k_offs[g] > c.t.fused_max)
             return false;
     return true;
 }
-
-// LoRA-routed tokens from which lora_sgmv_delta folds the shrink's slabs
-// before the expand (measured: Llama-3-8B prefill, 12.6 K tokens, -3 %;
-// 3.6 K tokens, -5 %; a 0.8 K-token mixed batch, +3 %).
-constexpr int kDeltaFoldTokens = 2048;
 
 // Feature tiles of width f: F, nft and nf of the launch arguments.
 void set_fused_feat(const Common& c, FusedArgs& a, int f)
@@ -2037,13 +2071,14 @@ void set_fused_feat(const Common& c, FusedArgs& a, int f)
 }
 
 // The widest feature tile: the largest power of two <= kFusedMaxFeat
-// dividing every slice width (LORA_SGMV_FUSED_FEAT caps it, for tuning).
+// dividing every slice width (the fused_feature_tile option, a power of two
+// in [32, 512], caps it).  Slice widths are multiples of 32 here, so the
+// result is a power of two of at least 32.
 int fused_widest_feat(const Common& c)
 {
-    const int feat_env = env_int("LORA_SGMV_FUSED_FEAT", 0);
-    int F = feat_env > 0 ? std::min(std::max(feat_env, 32), kFusedMaxFeat) : kFusedMaxFeat;
+    int F = c.t.feat > 0 ? c.t.feat : kFusedMaxFeat;
     for (int sl = 0; sl < c.fs.n_s; ++sl)
-        while (c.fs.widths[sl] % F)
+        while (F > 32 && c.fs.widths[sl] % F)
             F >>= 1;
     return F;
 }
@@ -2059,7 +2094,7 @@ int fused_widest_feat(const Common& c)
 void fused_feature_tiles(const Common& c, FusedArgs& a, int64_t rows, bool hostt)
 {
     int F = a.F;
-    if (env_int("LORA_SGMV_FUSED_FEAT", 0) <= 0) {
+    if (c.t.feat <= 0) {
         const int per_xcd = device_cus() / kXcds;
         while (F > 128) {
             int nf2 = 0;
@@ -2099,7 +2134,7 @@ void fused_common_args(const Common& c, FusedArgs& a, const void* x, int64_t ldx
     a.n_s = c.fs.n_s;
     for (int i = 0; i < 5; ++i)
         a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
-    a.krot = env_int("LORA_SGMV_FUSED_KROT", 1);
+    a.krot = c.t.krot;
     a.kc = 0;
     a.slabs = nullptr;
     a.slab = 0;
@@ -2125,7 +2160,7 @@ int64_t fused_host_tiles(const Common& c)
 bool fused_tile_table(const Common& c, FusedArgs& a, int64_t& rows)
 {
     int order[LORA_MAX_HOST_GROUPS], cnt[kXcds] = {}, xcd_of[LORA_MAX_HOST_GROUPS];
-    const bool together = env_int("LORA_SGMV_XCD_GROUPS", 1) != 0;
+    constexpr bool together = true;
     for (int g = 0; g < c.r.G; ++g)
         order[g] = g;
     auto gtiles = [&](int g) { return (c.r.k_offs[g + 1] - c.r.k_offs[g] + kFusedTileM - 1) / kFusedTileM; };
@@ -2181,7 +2216,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
         rows = (tiles + kXcds - 1) / kXcds;
     fused_feature_tiles(c, a, rows, hostt);
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
-    const bool xlds = a.wave_steps <= kXLdsSteps && env_int("LORA_SGMV_FUSED_XLDS", 1);
+    const bool xlds = a.wave_steps <= kXLdsSteps;
     const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
     const bool gather = c.r.rows != nullptr;
 #define LORA_FUSED(NH, ST, XL)                                                             \
@@ -2217,12 +2252,11 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
 // the rank-space values).  On the Llama-3-8B decode batch: MLP down (K 14336)
 // 20.9 -> 10.2 us, gate_up (28 672 outputs) 24.6 -> 16.9 us; the attention
 // families stay on the one-kernel path (QKV 8.2 there, 10.3 us split).
-// LORA_SGMV_SPLITK_SHORT=0/1 forces the choice.
+// The splitk_short option (0/1) forces the choice.
 bool splitk_short_wanted(const Common& c)
 {
-    const int e = env_int("LORA_SGMV_SPLITK_SHORT", -1);
-    if (e >= 0)
-        return e > 0;
+    if (c.t.splitk_short >= 0)
+        return c.t.splitk_short > 0;
     if (c.fs.in_f > 4096)
         return true;
     int nf = 0;
@@ -2307,8 +2341,7 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
     const int64_t per_xcd = device_cus() / kXcds;
     int pairs = 1;
     if (F == kFusedMaxFeat && rows * b.nf > 2 * per_xcd) {
-        const int most = std::min(std::max(env_int("LORA_SGMV_EXPAND_PAIRS", 4), 1), 4);
-        for (int p = 2; p <= most; p *= 2) {
+        for (int p = 2; p <= 4; p *= 2) {
             bool fits = true;
             for (int sl = 0; sl < c.fs.n_s; ++sl)
                 fits = fits && c.fs.widths[sl] % (p * kFusedMaxFeat) == 0;
@@ -2354,10 +2387,76 @@ bool row_ok(int64_t ld, int64_t width, int elem)
 }
 
 // Under per-token routing one buffer resource spans all of x or y, and row
-// num_rows is the out-of-range row: every offset must fit 32 bits.
+// num_rows is the out-of-range row.  Masked lanes use offset kOOB = 2^31, so
+// the resource, out-of-range row included, must end below it: otherwise a
+// masked lane would read and write back a real row.
 bool rows_fit(const Common& c, int64_t ld)
 {
-    return !c.r.rows || ((int64_t)c.r.nrows + 1) * ld * c.fs.elem <= 0xFFFFFFFFLL;
+    return !c.r.rows || ((int64_t)c.r.nrows + 1) * ld * c.fs.elem <= (int64_t)kOOB;
+}
+
+// The delta of one family once the common arguments are checked: the
+// one-kernel path (or its split-K form, when a workspace is given and AUTO
+// wants it) or the two-kernel path through the workspace.
+lora_status_t run_delta(const Common& c, const void* x, int64_t ldx, const void* A_stack, const void* B_stack,
+                        const void* bias_stack, void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                        int32_t path, hipStream_t s)
+{
+    lora_status_t st;
+    // the one-kernel path touches no workspace, so it may be NULL there
+    const bool fused = path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c));
+    if (fused) {
+        if (path == LORA_PATH_AUTO && workspace && splitk_short_wanted(c)) {
+            st = run_splitk_short(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, workspace, workspace_bytes,
+                                  path, s);
+            if (st != LORA_ERR_UNSPECIFIED)
+                return st;
+        }
+        return run_fused(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
+    }
+    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
+    if (!workspace)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < delta_workspace(plan))
+        return LORA_ERR_CAPACITY;
+    float* slabs = reinterpret_cast<float*>(workspace);
+    st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
+    if (st != LORA_OK)
+        return st;
+    int S = plan.S;
+    const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
+    // Fold the slabs into slab 0 first on long batches: every feature tile
+    // of the expand would otherwise read all S slabs of its token tile, while
+    // the fold reads them once, for one extra launch of a few microseconds
+    // that only a long batch amortises.  The fold_slabs option forces it.
+    if (S > 1 && (c.t.fold > 0 || (c.t.fold < 0 && c.r.end >= kDeltaFoldTokens))) {
+        hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
+                           0, s, slabs, n4, S, slabs, n4);
+        if (hipGetLastError() != hipSuccess)
+            return LORA_ERR_DEVICE;
+        S = 1;
+    }
+    return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, bias_stack, y, ldy, path, s);
+}
+
+// Argument checks of both delta entry points (all before any launch).
+lora_status_t check_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx, const void* A_stack,
+                          const void* B_stack, const void* bias_stack, const lora_routing_t* routing,
+                          const void* y, int64_t ldy, int32_t path, const lora_options_t* options, Common* c)
+{
+    lora_status_t st = check_common(dims, family, path, routing, options, c);
+    if (st != LORA_OK)
+        return st;
+    if ((path == LORA_PATH_MFMA && !(shrink_mfma_ok(*c) && expand_mfma_ok(*c))) ||
+        (path == LORA_PATH_FUSED && !fused_ok(*c)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (c->r.end == 0 || c->r.G == 0)
+        return LORA_OK;
+    if (!x || !A_stack || !B_stack || !y || !row_ok(ldx, c->fs.in_f, c->fs.elem) ||
+        !row_ok(ldy, c->fs.out_f, c->fs.elem) || !rows_fit(*c, ldx) || !rows_fit(*c, ldy) || !aligned16(x) ||
+        !aligned16(y) || !aligned16(A_stack) || !aligned16(B_stack) || !aligned16(bias_stack))
+        return LORA_ERR_INVALID_ARGUMENT;
+    return LORA_OK;
 }
 
 }  // namespace
@@ -2372,7 +2471,7 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
                                void* workspace, size_t workspace_bytes, int32_t path, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, routing, &c);
+    lora_status_t st = check_common(dims, family, path, routing, nullptr, &c);
     if (st != LORA_OK)
         return st;
     if ((path == LORA_PATH_MFMA && !shrink_mfma_ok(c)) || path == LORA_PATH_FUSED)
@@ -2406,7 +2505,7 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
                                void* y, int64_t ldy, int32_t path, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, routing, &c);
+    lora_status_t st = check_common(dims, family, path, routing, nullptr, &c);
     if (st != LORA_OK)
         return st;
     if ((path == LORA_PATH_MFMA && !expand_mfma_ok(c)) || path == LORA_PATH_FUSED)
@@ -2422,52 +2521,17 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
 lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
                               const void* A_stack, const void* B_stack, const void* bias_stack,
                               const lora_routing_t* routing, void* y, int64_t ldy, void* workspace,
-                              size_t workspace_bytes, int32_t path, void* stream)
+                              size_t workspace_bytes, int32_t path, const lora_options_t* options, void* stream)
 {
     Common c;
-    lora_status_t st = check_common(dims, family, path, routing, &c);
-    if (st != LORA_OK)
+    lora_status_t st =
+        check_delta(dims, family, x, ldx, A_stack, B_stack, bias_stack, routing, y, ldy, path, options, &c);
+    if (st != LORA_OK || c.r.end == 0 || c.r.G == 0)
         return st;
-    if ((path == LORA_PATH_MFMA && !(shrink_mfma_ok(c) && expand_mfma_ok(c))) ||
-        (path == LORA_PATH_FUSED && !fused_ok(c)))
+    if (!aligned16(workspace))
         return LORA_ERR_INVALID_ARGUMENT;
-    if (c.r.end == 0 || c.r.G == 0)
-        return LORA_OK;
-    if (!x || !A_stack || !B_stack || !y || !workspace || !row_ok(ldx, c.fs.in_f, c.fs.elem) ||
-        !row_ok(ldy, c.fs.out_f, c.fs.elem) || !rows_fit(c, ldx) || !rows_fit(c, ldy) || !aligned16(x) ||
-        !aligned16(y) || !aligned16(A_stack) ||
-        !aligned16(B_stack) || !aligned16(workspace) || !aligned16(bias_stack))
-        return LORA_ERR_INVALID_ARGUMENT;
-    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
-    if (workspace_bytes < delta_workspace(plan))
-        return LORA_ERR_CAPACITY;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (path == LORA_PATH_AUTO && fused_auto(c) && splitk_short_wanted(c)) {
-        st = run_splitk_short(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, workspace, workspace_bytes, path, s);
-        if (st != LORA_ERR_UNSPECIFIED)
-            return st;
-    }
-    if (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c)))
-        return run_fused(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
-    float* slabs = reinterpret_cast<float*>(workspace);
-    st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
-    if (st != LORA_OK)
-        return st;
-    int S = plan.S;
-    const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
-    // Fold the slabs into slab 0 first on long batches: every feature tile
-    // of the expand would otherwise read all S slabs of its token tile, while
-    // the fold reads them once, for one extra launch of a few microseconds
-    // that only a long batch amortises.  LORA_SGMV_DELTA_REDUCE=0/1 forces it.
-    const int fold = env_int("LORA_SGMV_DELTA_REDUCE", -1);
-    if (S > 1 && (fold > 0 || (fold < 0 && c.r.end >= kDeltaFoldTokens))) {
-        hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
-                           0, s, slabs, n4, S, slabs, n4);
-        if (hipGetLastError() != hipSuccess)
-            return LORA_ERR_DEVICE;
-        S = 1;
-    }
-    return run_expand(c, slabs, (int64_t)c.r.end * c.fs.C, S, B_stack, bias_stack, y, ldy, path, s);
+    return run_delta(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, workspace, workspace_bytes, path,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 // Bytes of one slot of each stack: A_qkv, B_qkv, A_o, B_o.

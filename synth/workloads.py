@@ -193,10 +193,14 @@ def draw_bias(w: Workload, layer: int, slot: int, projections=PROJECTIONS) -> Di
 
 
 def _to_dtype_values(a: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 draws rounded to the nearest bf16 number (ties to even) when the
+    workload is bf16; the draws are finite, so no NaN or overflow case."""
     if dtype == "f32":
         return a
-    # clear the low 16 bits: the value is then exactly a bf16 number
-    return (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    keep_odd = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + keep_odd) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def draw_activations(w: Workload, layer: int, n_tokens: int) -> Dict[str, np.ndarray]:

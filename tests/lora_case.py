@@ -43,10 +43,11 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def pack_stacks(w: synth.Workload, layer: int, ranks: np.ndarray, targets="qkvo",
-                zero_B: bool = False) -> Dict[str, np.ndarray]:
+                zero_B: bool = False, with_ref: bool = True) -> Dict[str, np.ndarray]:
     """Stacks [L, ...] of one layer: A_qkv / B_qkv / A_o / B_o packed by the
-    product library (device layout, for the GPU) and, under "ref", the same
-    adapters packed by the oracle (logical layout, for the reference)."""
+    product library (device layout, for the GPU) and, under "ref" (unless
+    with_ref is false), the same adapters packed by the oracle (logical
+    layout, for the reference)."""
     d = dims_of(w)
     out = {k: [] for k in ("A_qkv", "B_qkv", "A_o", "B_o")}
     ref = {k: [] for k in out}
@@ -55,13 +56,16 @@ def pack_stacks(w: synth.Workload, layer: int, ranks: np.ndarray, targets="qkvo"
         if zero_B:
             weights = {p: (a, np.zeros_like(b)) for p, (a, b) in weights.items()}
         pk = srg.lora_pack_adapter(d, int(ranks[s]), w.lora_alpha, w.use_rslora, True, targets, weights)
-        po = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank, w.dtype,
-                                 int(ranks[s]), w.lora_alpha, w.use_rslora, True, targets, weights)
         for k in out:
             out[k].append(pk[k])
-            ref[k].append(po[k])
+        if with_ref:
+            po = oracle.pack_adapter(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank, w.dtype,
+                                     int(ranks[s]), w.lora_alpha, w.use_rslora, True, targets, weights)
+            for k in ref:
+                ref[k].append(po[k])
     stacks = {k: np.stack(v) for k, v in out.items()}
-    stacks["ref"] = {k: np.stack(v) for k, v in ref.items()}
+    if with_ref:
+        stacks["ref"] = {k: np.stack(v) for k, v in ref.items()}
     return stacks
 
 
@@ -152,10 +156,11 @@ class GpuLayer:
             self.ws[fam] = torch.full((max(nb, 16) // 4 + 4,), -1, dtype=torch.int32, device="cuda")
 
     def run(self, path: int = srg.PATH_AUTO, families=(srg.FAMILY_QKV, srg.FAMILY_O),
-            fused: bool = False, routing: str = "host"):
+            fused: bool = False, routing: str = "host", options=None):
         """fused=False: lora_sgmv_shrink then lora_sgmv_expand (u checked);
-        fused=True: lora_sgmv_delta (u stays internal).  routing: "host"
-        (host copies passed, kernel-argument routing) or "device"."""
+        fused=True: lora_sgmv_delta (u stays internal), with `options`
+        (srg.LoraOptions or None).  routing: "host" (host copies passed,
+        kernel-argument routing) or "device"."""
         rt = self.routing[routing]
         for fam in families:
             xk, yk = ("x_qkv", "y_qkv") if fam == srg.FAMILY_QKV else ("x_o", "y_o")
@@ -166,7 +171,7 @@ class GpuLayer:
                 log(f"  launch delta family={fam} path={path} routing={routing} end={self.end} G={self.G}"
                     f" bias={bias is not None}")
                 srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path,
-                                    bias=bias)
+                                    bias=bias, options=options)
                 continue
             log(f"  launch shrink+expand family={fam} path={path} routing={routing} end={self.end} G={self.G}"
                 f" bias={bias is not None}")

@@ -28,7 +28,7 @@ def mdims(w):
                         w.dtype, w.intermediate)
 
 
-def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0, with_bias=False):
+def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0, with_bias=False, options=None):
     import torch
     d = mdims(w)
     in_f, n_s, widths, out_f = srg.lora_family_shape(d, fam)
@@ -65,7 +65,7 @@ def run_family(w, fam, lengths, slots, ranks, path, fused, layer=0, with_bias=Fa
     bs = to_dev(np.stack(bl), w.dtype) if with_bias else None
     log(f"  mlp family={fam} path={path} fused={fused} T={T} end={end} G={rt['num_groups']} bias={with_bias}")
     if fused:
-        srg.lora_sgmv_delta(d, fam, x, As, Bs, routing, y, ws, PATHS[path], bias=bs)
+        srg.lora_sgmv_delta(d, fam, x, As, Bs, routing, y, ws, PATHS[path], bias=bs, options=options)
     else:
         u = torch.zeros((max(end, 1), n_s * w.max_lora_rank), dtype=torch.float32, device="cuda")
         srg.lora_sgmv_shrink(d, fam, x, As, routing, u, ws, PATHS[path])
@@ -133,7 +133,7 @@ def test_mlp_with_lora_bias(fam, fused, path):
 
 
 @pytest.mark.parametrize("fam", [srg.FAMILY_GATE_UP, srg.FAMILY_DOWN])
-def test_split_k_short_wide_and_long(fam, monkeypatch):
+def test_split_k_short_wide_and_long(fam):
     """The split-K delta for short groups at shapes past its tables: an
     intermediate width of 36 864 makes gate_up 73 728 features wide, more
     than 64 feature tiles of 1024, so its expand half falls back to the
@@ -144,7 +144,7 @@ def test_split_k_short_wide_and_long(fam, monkeypatch):
     # every group at most 32 tokens (slot 0: 1 + 30, slot 1: 24, slot 2: 16, slot 3: 0 + 3)
     lengths = np.array([1, 24, 16, 0, 9, 30, 3], np.int64)
     slots = np.array([0, 1, 2, 3, -1, 0, 3], np.int32)
-    monkeypatch.setenv("LORA_SGMV_SPLITK_SHORT", "1")
-    ey = run_family(w, fam, lengths, slots, np.full(w.max_num_loras, 16, np.int32), "auto", True)
+    ey = run_family(w, fam, lengths, slots, np.full(w.max_num_loras, 16, np.int32), "auto", True,
+                    options=srg.LoraOptions(splitk_short=1))
     log(f"[mlp] wide/long family={fam} y_rel={ey:.3e}")
     assert ey <= TOL["bf16"]

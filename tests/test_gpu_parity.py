@@ -2,7 +2,7 @@
 
 Workloads (synthetic, seeded; shapes of the pages' attention blocks):
 tiny (fp32), decode, prefill, mixed (bf16) at full size with every request
-checked; the 32-layer stack at full size with sampled rows of every layer.
+checked; the 32-layer stack at full size with every row of every layer.
 Every path (auto, VALU, MFMA) runs where it applies.  Edge cases: empty and
 base-only batches, the pages' base-only routing form, zero-length requests,
 ragged segment lengths around the tile size, zero B, rows at and past `end`,
@@ -54,7 +54,7 @@ def workload_case(name, layer=0):
 @pytest.mark.parametrize("api", ["split", "delta", "delta_reduce", "delta_nofold", "split_devroute"])
 @pytest.mark.parametrize("path", list(DELTA_PATHS))
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed"])
-def test_full_workload_parity(name, path, api, monkeypatch):
+def test_full_workload_parity(name, path, api):
     """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
     lora_sgmv_delta (AUTO takes the one-kernel path on decode batches);
     delta_reduce: lora_sgmv_delta on the two-kernel path with its slabs folded
@@ -70,41 +70,71 @@ def test_full_workload_parity(name, path, api, monkeypatch):
         pytest.skip("the one-kernel path exists for lora_sgmv_delta only")
     if path == "fused" and not fused_applies(w):
         pytest.skip("one-kernel path needs bf16 and rank 16 or 32 (error path tested separately)")
+    opts = None
     if api in ("delta_reduce", "delta_nofold"):
-        monkeypatch.setenv("LORA_SGMV_DELTA_REDUCE", "1" if api == "delta_reduce" else "0")
-        monkeypatch.setenv("LORA_SGMV_FUSED_MAX", "0")
+        opts = srg.LoraOptions(fused_max_tokens=0, fold_slabs=1 if api == "delta_reduce" else 0)
     log(f"[parity] workload={name} path={path} api={api} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts)
-    gl.run(DELTA_PATHS[path], fused=api.startswith("delta"), routing="device" if api.endswith("devroute") else "host")
+    gl.run(DELTA_PATHS[path], fused=api.startswith("delta"), routing="device" if api.endswith("devroute") else "host",
+           options=opts)
     ey, eu = compare(w, gl, ref, check_u=api.startswith("split"))
     log(f"[parity] workload={name} path={path} api={api} y_rel={ey:.3e} u_rel={eu:.3e}")
     assert ey <= TOL[w.dtype]
     assert eu <= U_TOL[w.dtype]
 
 
-def test_stack_layers_sampled():
-    """Layers of the 32-layer stack at full size (first, last and some in
-    between); up to 8 sampled rows of every request checked against the oracle."""
+def test_stack_every_row_every_layer(tmp_path):
+    """All 32 layers of the stack workload at full size (rsLoRA rank 32, 4096
+    tokens, the last 4 requests base), every row of every request of both
+    families against the oracle: 3 630 LoRA rows x (6 144 + 4 096) outputs
+    per layer, and every base row bit-identical.  Even layers run the split
+    calls (u checked too), odd layers lora_sgmv_delta; every third layer reads
+    the routing from the device arrays only.  The oracle runs in spawned
+    worker processes on the CPU (stack_check.py), which regenerate each
+    layer's inputs from its seeds, while this process runs the next layer on
+    the GPU."""
+    import multiprocessing as mp
+    import os
+    import stack_check
+
     w = synth.get_workload("stack")
     lengths, slots = synth.draw_requests(w)
     ranks = synth.draw_ranks(w)
     T = int(lengths.sum())
-    rng = np.random.default_rng(5)
-    worst = 0.0
-    for layer in (0, 1, 11, 22, w.n_layers - 2, w.n_layers - 1):
-        stacks = pack_stacks(w, layer, ranks)
-        acts = synth.draw_activations(w, layer, T)
-        rows = {i: np.unique(np.concatenate([[0, lengths[i] - 1], rng.integers(0, lengths[i], 6)]))
-                for i in range(len(lengths))}
-        log(f"[stack] layer={layer}")
-        gl = GpuLayer(w, stacks, lengths, slots, acts)
-        gl.run(srg.PATH_AUTO, fused=layer % 2 == 1, routing="device" if layer % 3 == 0 else "host")
-        ref = oracle_layer(w, stacks, lengths, slots, acts, token_rows=rows)
-        ey, eu = compare(w, gl, ref, check_u=layer % 2 == 0)
-        worst = max(worst, ey)
-        assert ey <= TOL[w.dtype], (layer, ey)
-        assert eu <= U_TOL[w.dtype], (layer, eu)
-    log(f"[stack] worst y_rel={worst:.3e}")
+    nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    log(f"[stack] {w.n_layers} layers, T={T}, oracle workers={nproc}")
+    results = []
+    with mp.get_context("spawn").Pool(nproc) as pool:
+        pending = []
+        for layer in range(w.n_layers):
+            stacks = pack_stacks(w, layer, ranks, with_ref=False)
+            acts = synth.draw_activations(w, layer, T)
+            split = layer % 2 == 0
+            gl = GpuLayer(w, stacks, lengths, slots, acts)
+            gl.run(srg.PATH_AUTO, fused=not split, routing="device" if layer % 3 == 0 else "host")
+            data = {"y_qkv": synth.bf16_bits(gl.y_arrival("y_qkv")), "y_o": synth.bf16_bits(gl.y_arrival("y_o"))}
+            if split:
+                data["u_qkv"] = gl.u_arrival(srg.FAMILY_QKV)
+                data["u_o"] = gl.u_arrival(srg.FAMILY_O)
+            path = str(tmp_path / f"layer{layer}.npz")
+            np.savez(path, **data)
+            del gl, data, acts
+            pending.append(pool.apply_async(stack_check.check_layer, (("stack", layer, path),)))
+            log(f"[stack] layer={layer} done on the GPU ({'split' if split else 'delta'})")
+        for p in pending:
+            r = p.get(timeout=900)
+            log(f"[stack] layer={r['layer']} y_rel qkv={r['y_rel_qkv']:.3e} o={r['y_rel_o']:.3e}"
+                f" u_rel qkv={r['u_rel_qkv']} o={r['u_rel_o']} rows={r['rows_qkv']}")
+            results.append(r)
+    assert len(results) == w.n_layers
+    lora_rows = int(lengths[slots >= 0].sum())
+    for r in results:
+        assert r["base_rows_identical"], r
+        assert r["rows_qkv"] == lora_rows and r["rows_o"] == lora_rows, r
+        assert r["y_rel_qkv"] <= TOL[w.dtype] and r["y_rel_o"] <= TOL[w.dtype], r
+        if r["layer"] % 2 == 0:
+            assert r["u_rel_qkv"] <= U_TOL[w.dtype] and r["u_rel_o"] <= U_TOL[w.dtype], r
+    log(f"[stack] worst y_rel={max(max(r['y_rel_qkv'], r['y_rel_o']) for r in results):.3e}")
 
 
 # ----------------------------------------------------------------------------- edge cases
@@ -382,7 +412,7 @@ def test_host_side_argument_errors_launch_nothing():
 
 
 @pytest.mark.parametrize("name", ["decode", "stack_decode"])
-def test_fused_launch_shapes_bit_identical(name, monkeypatch):
+def test_fused_launch_shapes_bit_identical(name):
     """The one-kernel delta's launch choices do not change its arithmetic:
     every feature tile width (128, 256 or 512 features per workgroup, or the
     launcher's own pick) and the wave K-range rotation on or off give the same
@@ -403,11 +433,10 @@ def test_fused_launch_shapes_bit_identical(name, monkeypatch):
     outs = {}
     for feat in ("", "512", "256", "128"):
         for krot in ("1", "0"):
-            monkeypatch.setenv("LORA_SGMV_FUSED_FEAT", feat)
-            monkeypatch.setenv("LORA_SGMV_FUSED_KROT", krot)
+            opts = srg.LoraOptions(fused_feature_tile=int(feat or 0), fused_k_rotation=int(krot))
             log(f"[fused-shapes] workload={name} feat={feat or 'auto'} krot={krot}")
             gl = GpuLayer(w, stacks, lengths, slots, acts)
-            gl.run(srg.PATH_FUSED, fused=True)
+            gl.run(srg.PATH_FUSED, fused=True, options=opts)
             ey, _ = compare(w, gl, ref, check_u=False)
             assert ey <= TOL[w.dtype], (feat, krot, ey)
             outs[(feat, krot)] = (gl.y_arrival("y_qkv"), gl.y_arrival("y_o"))
@@ -415,3 +444,19 @@ def test_fused_launch_shapes_bit_identical(name, monkeypatch):
     for key, (yq, yo) in outs.items():
         assert np.array_equal(yq.view(np.uint32), first[0].view(np.uint32)), key
         assert np.array_equal(yo.view(np.uint32), first[1].view(np.uint32)), key
+
+
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_one_kernel_delta_takes_a_null_workspace(path):
+    """The one-kernel path touches no workspace, so lora_sgmv_delta accepts
+    NULL there: the decode batch gives the same bits as with a workspace."""
+    w, lengths, slots, stacks, acts, ref = workload_case("decode")
+    a = GpuLayer(w, stacks, lengths, slots, acts)
+    a.run(DELTA_PATHS[path], fused=True)
+    b = GpuLayer(w, stacks, lengths, slots, acts)
+    b.ws = {k: None for k in b.ws}
+    b.run(DELTA_PATHS[path], fused=True)
+    ey, _ = compare(w, b, ref, check_u=False)
+    assert ey <= TOL[w.dtype]
+    for key in ("y_qkv", "y_o"):
+        assert np.array_equal(a.y_arrival(key).view(np.uint32), b.y_arrival(key).view(np.uint32))

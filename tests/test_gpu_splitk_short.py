@@ -3,7 +3,7 @@ runs the one-kernel delta's shrink half with K split over workgroups into
 fp32 slabs, then the expand kernel, when a batch has only short groups but
 the one-kernel launch would be slow (a long K, or a wide output).  The MLP
 decode batch takes it by default (test_gpu_mlp.py); here it is forced with
-LORA_SGMV_SPLITK_SHORT=1 onto the attention families and checked against the
+the splitk_short option onto the attention families and checked against the
 oracle: the Llama-3-8B decode batch, a rank-32 decode batch on the stack's
 adapters, ragged short groups with a LoRA bias, per-token routing with
 padded strided buffers."""
@@ -45,15 +45,14 @@ def decode_case(name):
 
 
 @pytest.mark.parametrize("name", ["decode", "stack_decode"])
-def test_forced_splitk_short_matches_oracle(name, monkeypatch):
+def test_forced_splitk_short_matches_oracle(name):
     w, lengths, slots, stacks, acts = decode_case(name)
     ref = oracle_layer(w, stacks, lengths, slots, acts)
     out = {}
     for mode in ("1", "0"):
-        monkeypatch.setenv("LORA_SGMV_SPLITK_SHORT", mode)
         log(f"[splitk-short] workload={name} forced={mode} T={int(lengths.sum())}")
         gl = GpuLayer(w, stacks, lengths, slots, acts)
-        gl.run(srg.PATH_AUTO, fused=True)
+        gl.run(srg.PATH_AUTO, fused=True, options=srg.LoraOptions(splitk_short=int(mode)))
         ey, _ = compare(w, gl, ref, check_u=False)
         log(f"[splitk-short] workload={name} forced={mode} y_rel={ey:.3e}")
         assert ey <= TOL[w.dtype], (mode, ey)
@@ -64,7 +63,7 @@ def test_forced_splitk_short_matches_oracle(name, monkeypatch):
 
 
 @pytest.mark.parametrize("R", [16, 32])
-def test_forced_splitk_short_ragged_with_bias(R, monkeypatch):
+def test_forced_splitk_short_ragged_with_bias(R):
     """Short groups of 1..32 tokens (ragged tiles of the 16-token table, an
     empty request, base requests in between) with a LoRA bias."""
     base = synth.get_workload("decode")
@@ -72,13 +71,12 @@ def test_forced_splitk_short_ragged_with_bias(R, monkeypatch):
                           "max_lora_rank": R, "max_num_loras": 6})
     lengths = np.array([1, 15, 16, 17, 31, 32, 0, 3, 9, 24, 2], np.int64)
     slots = np.array([0, 1, 2, 3, 4, 5, 2, -1, 0, 1, -1], np.int32)
-    monkeypatch.setenv("LORA_SGMV_SPLITK_SHORT", "1")
     stacks = pack_stacks(w, 0, np.full(w.max_num_loras, min(8, R), np.int32))
     bias = pack_bias_stacks(w, 0)
     acts = synth.draw_activations(w, 0, int(lengths.sum()))
     log(f"[splitk-short] ragged R={R} T={int(lengths.sum())}")
     gl = GpuLayer(w, stacks, lengths, slots, acts, pad_rows=5, pad_cols=16, bias=bias)
-    gl.run(srg.PATH_AUTO, fused=True)
+    gl.run(srg.PATH_AUTO, fused=True, options=srg.LoraOptions(splitk_short=1))
     ey, _ = compare(w, gl, oracle_layer(w, stacks, lengths, slots, acts, bias=bias), check_u=False)
     log(f"[splitk-short] ragged R={R} y_rel={ey:.3e}")
     assert ey <= TOL[w.dtype]
@@ -90,14 +88,14 @@ def test_forced_splitk_short_ragged_with_bias(R, monkeypatch):
         assert np.all(full[:, width:] == 0.0)
 
 
-def test_forced_splitk_short_per_token_routing(monkeypatch):
+def test_forced_splitk_short_per_token_routing():
     """Per-token routing (x gathered, y scattered through the sorted token
     indices) on the decode batch with its slots shuffled over the batch."""
     import test_gpu_token_routing as tr
-    monkeypatch.setenv("LORA_SGMV_SPLITK_SHORT", "1")
     w, token_slot, stacks, acts = tr.token_case("decode", True)
     log(f"[splitk-short] per-token routing T={len(token_slot)}")
-    ys, _ = tr.run_tokens(w, stacks, token_slot, acts, "auto", "delta", pad_rows=3, pad_cols=8)
+    ys, _ = tr.run_tokens(w, stacks, token_slot, acts, "auto", "delta", pad_rows=3, pad_cols=8,
+                          options=srg.LoraOptions(splitk_short=1))
     ey = tr.check(w, stacks, token_slot, acts, ys, pad_rows=3, pad_cols=8)
     log(f"[splitk-short] per-token routing y_rel={ey:.3e}")
     assert ey <= TOL[w.dtype]

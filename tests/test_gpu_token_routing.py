@@ -35,7 +35,8 @@ def dims_of(w):
     return srg.LoraDims(w.hidden, w.n_heads, w.n_kv_heads, w.head_dim, w.max_lora_rank, w.max_num_loras, w.dtype)
 
 
-def run_tokens(w, stacks, token_slot, acts, path, api, routing="host", bias=None, pad_rows=0, pad_cols=0):
+def run_tokens(w, stacks, token_slot, acts, path, api, routing="host", bias=None, pad_rows=0, pad_cols=0,
+               options=None):
     """Runs both families with per-token routing; returns y of both families
     in token order (with the padding rows) and the routing."""
     d = dims_of(w)
@@ -62,7 +63,7 @@ def run_tokens(w, stacks, token_slot, acts, path, api, routing="host", bias=None
         log(f"  tokens family={fam} path={path} api={api} routing={routing} T={T} end={end} "
             f"G={rt['num_groups']} bias={b is not None} pad={pad_rows},{pad_cols}")
         if api == "delta":
-            srg.lora_sgmv_delta(d, fam, x, st[ak], st[bk], r, y, ws, PATHS[path], bias=b)
+            srg.lora_sgmv_delta(d, fam, x, st[ak], st[bk], r, y, ws, PATHS[path], bias=b, options=options)
         else:
             u = torch.full((max(end, 1), n_s * w.max_lora_rank), float("nan"), dtype=torch.float32,
                            device="cuda")

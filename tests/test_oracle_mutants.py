@@ -1,8 +1,10 @@
 """Sensitivity of the oracle pins: plant one plausible mistake at a time in a
-copy of the oracle's C source (on the CPU), build it, and check that the pin
-suite then fails.  The committed oracle source is never modified."""
+copy of the oracle's C source or of its Python driver (on the CPU), build or
+load the copy, and check that the pin suite then fails.  The committed oracle
+source is never modified."""
 
 import os
+import shutil
 import subprocess
 import sys
 
@@ -45,3 +47,43 @@ def test_planted_mistake_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+# mistakes in the Python side of the oracle (oracle/oracle.py): the bf16
+# decoder every bf16 reference value passes through
+PY_MUTANTS = {
+    "bf16_decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "bf16_decode_sign_lost": ("b = np.ascontiguousarray(bits, dtype=np.uint16)",
+                              "b = np.ascontiguousarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)"),
+    "f32_stack_rounded": ('return bf16_to_f64(a) if dtype == "bf16" else np.asarray(a, dtype=np.float64)',
+                          'return bf16_to_f64(a) if dtype == "bf16" else np.asarray(a, dtype=np.float16).astype(np.float64)'),
+}
+
+
+@pytest.mark.parametrize("name", ["unchanged"] + sorted(PY_MUTANTS))
+def test_planted_python_mistake_is_caught(name, tmp_path):
+    """"unchanged" is the control: the copied, unmutated package passes."""
+    import oracle
+    lib = oracle.library_path()
+    if not os.path.exists(lib):
+        oracle.build()
+    old, new = PY_MUTANTS.get(name, ("def bf16_to_f64(", "def bf16_to_f64("))
+    pkg = tmp_path / "oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), pkg, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    src = (pkg / "oracle.py").read_text()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found"
+    (pkg / "oracle.py").write_text(src.replace(old, new))
+    # the mutated package first on the path, the repository after it (so the
+    # test suite's conftest does not put the real package in front)
+    code = ("import sys, pytest; sys.path[:0] = [%r, %r]; import oracle; "
+            "print('ORACLE_FROM', oracle.__file__, flush=True); "
+            "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r]))"
+            % (str(tmp_path), ROOT, os.path.join(ROOT, "tests", "test_oracle_pins.py")))
+    env = dict(os.environ, ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert f"ORACLE_FROM {pkg}" in r.stdout, r.stdout[-2000:]
+    if name == "unchanged":
+        assert r.returncode == 0, r.stdout[-2000:]
+    else:
+        assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

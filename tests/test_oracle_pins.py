@@ -97,6 +97,57 @@ def test_bf16_round_matches_torch():
     assert np.array_equal(got, want)
 
 
+def test_bf16_decoder_fixed_values():
+    """The oracle's bf16 decoder (the inverse of the pack's final cast,
+    [MAX-lora] 加载时的处理管线) on patterns whose values follow from the
+    bf16 format by hand: sign, 8 exponent bits (bias 127), 7 fraction bits."""
+    pats = np.array([0x3F80, 0xC020, 0x8000, 0x0000, 0x0001, 0x8001, 0x0080, 0x7F7F, 0x7F80, 0xFF80,
+                     0x4049, 0x3E80, 0x3F81], dtype=np.uint16)
+    want = [1.0, -2.5, -0.0, 0.0, 2.0 ** -133, -(2.0 ** -133), 2.0 ** -126, (2 - 2 ** -7) * 2.0 ** 127,
+            math.inf, -math.inf, 3.140625, 0.25, 1 + 2 ** -7]
+    got = oracle.bf16_to_f64(pats)
+    assert got.dtype == np.float64
+    for g, w_, bits in zip(got, want, pats):
+        assert g == w_, hex(bits)
+        assert math.copysign(1.0, g) == math.copysign(1.0, w_), hex(bits)
+    nan = oracle.bf16_to_f64(np.array([0x7FC0, 0xFFC1, 0x7F81], np.uint16))
+    assert np.all(np.isnan(nan))
+
+
+def test_bf16_decoder_every_pattern_matches_torch():
+    """All 65 536 bf16 patterns decode to the value torch's bfloat16 -> float64
+    conversion gives (a library routine); NaN patterns stay NaN."""
+    torch = pytest.importorskip("torch")
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(pats.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_to_f64(pats)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), want[~nan].view(np.uint64))
+
+
+def test_bf16_decoder_inverts_the_rounding_on_random_values():
+    """decode(round(v)) is the bf16 value nearest v: within half an ulp of
+    v (2^-9 relative), and torch's cast of v to bfloat16 gives the same
+    number, on 10^5 draws across magnitudes."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    v = (rng.standard_normal(100000) * np.exp(rng.uniform(-30, 30, 100000))).astype(np.float32)
+    dec = oracle.bf16_to_f64(oracle.bf16_round(v))
+    assert np.all(np.abs(dec - v.astype(np.float64)) <= np.abs(v.astype(np.float64)) * 2.0 ** -8)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(dec, ref)
+
+
+def test_stack_to_f64_by_dtype():
+    """bf16 stacks decode their patterns; fp32 stacks widen exactly."""
+    pats = np.array([[0x3F80, 0xC020]], np.uint16)
+    assert oracle.stack_to_f64(pats, "bf16").tolist() == [[1.0, -2.5]]
+    f = np.array([1.5, -3.0e-40, 3.4028235e38], np.float32)
+    got = oracle.stack_to_f64(f, "f32")
+    assert got.dtype == np.float64 and got.tolist() == [float(v) for v in f]
+
+
 def test_bf16_round_nan_stays_nan():
     bits = np.array([0x7FC00000, 0x7F800001, 0xFFA00000], dtype=np.uint32)
     got = oracle.bf16_round(bits.view(np.float32))
