@@ -411,6 +411,30 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
                               void* stream);
 
 /* ---------------------------------------------------------------------------
+ * lora_sgmv_delta_noalloc — device, asynchronous on `stream`.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * lora_sgmv_delta with the same arguments minus the workspace, whose partial
+ * sums go to a scratch array of lora_sgmv_noalloc_scratch_bytes() bytes
+ * (64 MiB) that the library holds in each device's memory while it is loaded.
+ * The call allocates and frees nothing.  A batch whose two-kernel path needs
+ * more partial-sum space than the scratch holds gets LORA_ERR_CAPACITY
+ * before any launch (lora_sgmv_workspace_bytes gives the need); the
+ * one-kernel path needs none.  Every call on one device shares that
+ * device's scratch, which keeps the last call's contents (every element a
+ * call reads it has written first, so no clearing is needed): calls that
+ * may overlap on one device (different streams, or host threads) race and
+ * must be ordered by the caller.  LORA_ERR_DEVICE if the scratch's device
+ * address cannot be obtained.
+ */
+size_t lora_sgmv_noalloc_scratch_bytes(void);
+lora_status_t lora_sgmv_delta_noalloc(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
+                                      const void* A_stack, const void* B_stack, const void* bias_stack,
+                                      const lora_routing_t* routing, void* y, int64_t ldy, int32_t path,
+                                      const lora_options_t* options, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Adapter slot cache — host, synchronous.
  *
  * Which adapter (a caller-chosen integer id >= 0, like vLLM's lora_int_id)

@@ -41,6 +41,8 @@ from ._lib import (  # noqa: F401
     lora_pack_family,
     lora_pack_bias,
     lora_sgmv_delta,
+    lora_sgmv_delta_noalloc,
+    lora_sgmv_noalloc_scratch_bytes,
     lora_sgmv_expand,
     lora_sgmv_shrink,
     lora_sgmv_workspace_bytes,

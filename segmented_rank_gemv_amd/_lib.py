@@ -190,6 +190,11 @@ def _load():
     lib.lora_sgmv_delta.restype = i32
     lib.lora_sgmv_delta.argtypes = [D, i32, P, i64, P, P, P, RT, P, i64, P, ctypes.c_size_t, i32,
                                     ctypes.POINTER(_LoraOptions), P]
+    lib.lora_sgmv_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.lora_sgmv_noalloc_scratch_bytes.argtypes = []
+    lib.lora_sgmv_delta_noalloc.restype = i32
+    lib.lora_sgmv_delta_noalloc.argtypes = [D, i32, P, i64, P, P, P, RT, P, i64, i32,
+                                            ctypes.POINTER(_LoraOptions), P]
     lib.lora_pack_bias.restype = i32
     lib.lora_pack_bias.argtypes = [D, i32, u32, P, P]
     I32P, I64P = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -487,6 +492,25 @@ def lora_sgmv_delta(dims: LoraDims, family: int, x, A_stack, B_stack, routing: L
                                     _dev_ptr(workspace, "workspace"), ws_bytes, int(path), oc,
                                     _stream_handle(stream)),
            "lora_sgmv_delta")
+
+
+def lora_sgmv_noalloc_scratch_bytes() -> int:
+    """Bytes of the device scratch array lora_sgmv_delta_noalloc uses."""
+    return int(_load().lora_sgmv_noalloc_scratch_bytes())
+
+
+def lora_sgmv_delta_noalloc(dims: LoraDims, family: int, x, A_stack, B_stack, routing: LoraRouting, y,
+                            path: int = PATH_AUTO, stream=None, bias=None,
+                            options: Optional[LoraOptions] = None) -> None:
+    """lora_sgmv_delta without a workspace argument: the partial sums go to
+    the library's own device scratch array; nothing is allocated."""
+    dc, rc = dims.c(), routing.c()
+    oc = None if options is None else ctypes.byref(options.c())
+    _check(_load().lora_sgmv_delta_noalloc(ctypes.byref(dc), family, _dev_ptr(x, "x"), _row_stride(x, "x"),
+                                            _dev_ptr(A_stack, "A_stack"), _dev_ptr(B_stack, "B_stack"),
+                                            _dev_ptr(bias, "bias"), ctypes.byref(rc), _dev_ptr(y, "y"),
+                                            _row_stride(y, "y"), int(path), oc, _stream_handle(stream)),
+           "lora_sgmv_delta_noalloc")
 
 
 def packed_to_torch(a: np.ndarray):

@@ -34,9 +34,19 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <string.h>
 
 #include "lora_internal.h"
+
+// Scratch of lora_sgmv_delta_noalloc: the partial sums that lora_sgmv_delta
+// keeps in the caller's workspace, in a device array of fixed size instead
+// (each device holds its own copy while the library is loaded).  In host
+// code `scratch` names a host-side stand-in, not a device address: the
+// array's address on a device comes from hipGetSymbolAddress with that
+// device current, once per device, and only that address reaches kernels.
+static constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
 
 #ifndef LORA_SHRINK_KC
 #define LORA_SHRINK_KC 128
@@ -2459,6 +2469,27 @@ lora_status_t check_delta(const lora_dims_t* dims, int32_t family, const void* x
     return LORA_OK;
 }
 
+constexpr size_t kScratchBytes = kNoallocScratchBytes;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (null on failure).
+void* scratch_address()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 }  // namespace lora
 
@@ -2531,6 +2562,29 @@ lora_status_t lora_sgmv_delta(const lora_dims_t* dims, int32_t family, const voi
     if (!aligned16(workspace))
         return LORA_ERR_INVALID_ARGUMENT;
     return run_delta(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, workspace, workspace_bytes, path,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t lora_sgmv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+lora_status_t lora_sgmv_delta_noalloc(const lora_dims_t* dims, int32_t family, const void* x, int64_t ldx,
+                                      const void* A_stack, const void* B_stack, const void* bias_stack,
+                                      const lora_routing_t* routing, void* y, int64_t ldy, int32_t path,
+                                      const lora_options_t* options, void* stream)
+{
+    Common c;
+    lora_status_t st =
+        check_delta(dims, family, x, ldx, A_stack, B_stack, bias_stack, routing, y, ldy, path, options, &c);
+    if (st != LORA_OK || c.r.end == 0 || c.r.G == 0)
+        return st;
+    // the two-kernel path's partial sums must fit the scratch array
+    const bool fused = path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c));
+    if (!fused && delta_workspace(plan_shrink(c.fs, c.r.end, c.r.G)) > kScratchBytes)
+        return LORA_ERR_CAPACITY;
+    void* ws = scratch_address();
+    if (!ws)
+        return LORA_ERR_DEVICE;
+    return run_delta(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, ws, kScratchBytes, path,
                      reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -156,11 +156,12 @@ class GpuLayer:
             self.ws[fam] = torch.full((max(nb, 16) // 4 + 4,), -1, dtype=torch.int32, device="cuda")
 
     def run(self, path: int = srg.PATH_AUTO, families=(srg.FAMILY_QKV, srg.FAMILY_O),
-            fused: bool = False, routing: str = "host", options=None):
+            fused: bool = False, routing: str = "host", options=None, noalloc: bool = False):
         """fused=False: lora_sgmv_shrink then lora_sgmv_expand (u checked);
         fused=True: lora_sgmv_delta (u stays internal), with `options`
-        (srg.LoraOptions or None).  routing: "host" (host copies passed,
-        kernel-argument routing) or "device"."""
+        (srg.LoraOptions or None), or with noalloc lora_sgmv_delta_noalloc.
+        routing: "host" (host copies passed, kernel-argument routing) or
+        "device"."""
         rt = self.routing[routing]
         for fam in families:
             xk, yk = ("x_qkv", "y_qkv") if fam == srg.FAMILY_QKV else ("x_o", "y_o")
@@ -169,9 +170,13 @@ class GpuLayer:
             bias = None if self.bias is None else self.bias["bias_qkv" if fam == srg.FAMILY_QKV else "bias_o"]
             if fused:
                 log(f"  launch delta family={fam} path={path} routing={routing} end={self.end} G={self.G}"
-                    f" bias={bias is not None}")
-                srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path,
-                                    bias=bias, options=options)
+                    f" bias={bias is not None} noalloc={noalloc}")
+                if noalloc:
+                    srg.lora_sgmv_delta_noalloc(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], path,
+                                                bias=bias, options=options)
+                else:
+                    srg.lora_sgmv_delta(self.dims, fam, self.dev[xk], A, B, rt, self.dev[yk], self.ws[fam], path,
+                                        bias=bias, options=options)
                 continue
             log(f"  launch shrink+expand family={fam} path={path} routing={routing} end={self.end} G={self.G}"
                 f" bias={bias is not None}")
