@@ -57,6 +57,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 UPLOAD_PIECE = 4096  # int32 entries per host-to-device copy of the token indices
+GRAPH_CALLS = 16     # least calls per captured graph when timing one call kind
+PREFILL_LAYERS = 4   # layer replicas of the prefill leg of the default run
 
 
 def parse():
@@ -78,6 +80,8 @@ def parse():
                    help="kernels read the routing from device memory only (no host copies)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the prefill leg that the default (decode) run also measures")
     p.add_argument("--counters", metavar="KIND", default=None,
                    help="counter-collection run: a plain copy of COPY_MIB MiB (calibration), then the "
                         "call KIND (e.g. delta_qkv) over every layer twice; no timing, no JSON line")
@@ -151,28 +155,13 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        summarize_traffic(args)
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this benchmark measures one GPU; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
-        sys.exit(2)
-
-    import torch
-    import synth
-    import segmented_rank_gemv_amd as srg
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
+def run_workload(args, torch, synth, srg, dev, log):
+    """One workload on the GPU: pack its adapters, lay out its layers, time
+    args.steps whole steps (phase 1) and every call kind (phase 2).  Returns
+    the measurements and the objects the extra legs reuse, or None for a
+    counter-collection run."""
     path = {"auto": srg.PATH_AUTO, "valu": srg.PATH_VALU, "mfma": srg.PATH_MFMA,
             "fused": srg.PATH_FUSED}[args.path]
-
     w = synth.get_workload(args.workload)
     n_layers = args.layers or REPLICAS[args.workload]
     if args.workload == "stack" and not args.layers:
@@ -194,7 +183,6 @@ def main():
     L, R = w.max_num_loras, w.max_lora_rank
     bf16 = w.dtype == "bf16"
     tdt = torch.bfloat16 if bf16 else torch.float32
-    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
 
     # routing once to lay the batch out in sorted order (the serving layer
     # sorts its batch once; the timed steps still route on the host)
@@ -328,7 +316,7 @@ def main():
                     call(args.counters, ly)
         torch.cuda.synchronize()
         log(f"counters: copy {COPY_MIB} MiB x 3, {args.counters} x {2 * n_layers}")
-        return
+        return None
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -378,14 +366,19 @@ def main():
     # reaches it, so the events time the kernels and not the host's launch
     # rate.
     ev_reps = max(1, min(args.steps, 20))
+    # at least GRAPH_CALLS calls per captured graph (passes over the layers
+    # repeated), so that the graph launch itself is a small part of each
+    # timed sequence
+    passes = max(1, -(-GRAPH_CALLS // n_layers)) if graph is not None else 1
     total_ms = {k: 0.0 for k in KINDS}
     kind_graphs = {}
     if graph is not None:
         for kind in KINDS:
             kg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(kg, stream=stream):
-                for ly in layers:
-                    call(kind, ly)
+                for _ in range(passes):
+                    for ly in layers:
+                        call(kind, ly)
             kind_graphs[kind] = kg
         torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -416,7 +409,7 @@ def main():
                 b.record()
                 torch.cuda.synchronize()
                 total_ms[kind] += a.elapsed_time(b)
-    avg_us = {k: 1e3 * total_ms[k] / (ev_reps * n_layers) for k in KINDS}
+    avg_us = {k: 1e3 * total_ms[k] / (ev_reps * n_layers * (passes if k in kind_graphs else 1)) for k in KINDS}
     log("phase 2: " + " ".join(f"{k}={v:.2f}us" for k, v in avg_us.items()))
 
     # algorithmic bytes per call (u, the rank-space intermediate, counted for
@@ -454,6 +447,70 @@ def main():
     value = end * n_layers / (ms_per_step * 1e-3)
     e2e_gbs = fam_bytes * n_layers / (ms_per_step * 1e-3) / 1e9
 
+    del kind_graphs, graph
+    return {"w": w, "n_layers": n_layers, "mlp": mlp, "dims": dims, "FAMS": FAMS, "lengths": lengths,
+            "slots": slots, "ranks": ranks, "offsets": offsets, "T": T, "L": L, "R": R, "bf16": bf16,
+            "end": end, "G": G, "fam_shape": fam_shape, "proj_desc": proj_desc, "layers": layers,
+            "stream": stream, "ms_per_step": ms_per_step, "host_route_s": host_route_s[0], "KINDS": KINDS,
+            "avg_us": avg_us, "kbytes": kbytes, "kflops": kflops, "fam_bytes": fam_bytes, "dominant": dominant,
+            "achieved": achieved, "traffic": traffic, "value": value, "e2e_gbs": e2e_gbs, "t_pack": t_pack,
+            "n_pack": n_pack, "graph_calls": passes * n_layers}
+
+
+def main():
+    args = parse()
+    if args.traffic_from:
+        summarize_traffic(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark measures one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import segmented_rank_gemv_amd as srg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    ctx = run_workload(args, torch, synth, srg, dev, log)
+    if ctx is None:
+        return
+    w, n_layers, mlp, dims, FAMS = ctx["w"], ctx["n_layers"], ctx["mlp"], ctx["dims"], ctx["FAMS"]
+    lengths, slots, ranks, offsets, T = ctx["lengths"], ctx["slots"], ctx["ranks"], ctx["offsets"], ctx["T"]
+    L, R, bf16, end, G = ctx["L"], ctx["R"], ctx["bf16"], ctx["end"], ctx["G"]
+    fam_shape, proj_desc, layers, stream = ctx["fam_shape"], ctx["proj_desc"], ctx["layers"], ctx["stream"]
+    KINDS, avg_us, kbytes, kflops = ctx["KINDS"], ctx["avg_us"], ctx["kbytes"], ctx["kflops"]
+    dominant, achieved, traffic = ctx["dominant"], ctx["achieved"], ctx["traffic"]
+    ms_per_step, value, e2e_gbs = ctx["ms_per_step"], ctx["value"], ctx["e2e_gbs"]
+
+    # ---- the prefill workload beside the decode headline (default run only):
+    # the same call through lora_sgmv_delta on the Llama-3-8B prefill batch
+    prefill = None
+    if (args.workload == "decode" and not args.no_prefill and not args.layers and not args.bias
+            and not args.token_routing and not args.device_routing and args.path == "auto" and args.api == "delta"):
+        pargs = argparse.Namespace(**{**vars(args), "workload": "prefill", "layers": PREFILL_LAYERS,
+                                      "steps": min(args.steps, 40), "warmup": min(args.warmup, 5)})
+        pre = run_workload(pargs, torch, synth, srg, dev, log)
+        prefill = {"workload": "prefill", "lora_tokens": pre["end"], "tokens": pre["T"], "groups": pre["G"],
+                   "layers_per_step": pre["n_layers"], "ms_per_step": pre["ms_per_step"],
+                   "value": pre["value"], "unit": "LoRA tokens x layers / s (q/k/v/o delta)",
+                   "end_to_end_GBps": pre["e2e_gbs"], "frac": pre["e2e_gbs"] / HBM_PEAK_GBS,
+                   "calls": {k: {"avg_us": pre["avg_us"][k], "bytes": pre["kbytes"][k],
+                                 "GBps": pre["kbytes"][k] / (pre["avg_us"][k] * 1e-6) / 1e9,
+                                 "frac": pre["kbytes"][k] / (pre["avg_us"][k] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                             for k in pre["KINDS"]},
+                   "calls_per_timed_graph": pre["graph_calls"]}
+        log(f"prefill: {pre['ms_per_step']:.4f} ms/step ({PREFILL_LAYERS} layers), "
+            + " ".join(f"{k}={v['avg_us']:.2f}us ({v['frac']:.3f})" for k, v in prefill["calls"].items()))
+        del pre
+        torch.cuda.empty_cache()
+
     # ---- reference streams (outside the step): what plain device kernels
     # reach on this GPU, beside the 8 TB/s nameplate -- an in-place add over
     # 1 GiB of bf16 (read + write, like the expand's y) and a row-wise max
@@ -481,6 +538,43 @@ def main():
                       "bytes": nbytes}
         del big, rows2d
         torch.cuda.empty_cache()
+        # launch-sized legs: one in-place add per launch moving as many bytes
+        # (read + write) as one call of each kind of the headline workload,
+        # over 64 rotating buffers, captured in one graph: what a single
+        # plain launch over that many bytes reaches here
+        legs = {}
+        for kind in KINDS:
+            moved = kbytes[kind]
+            elems = max(8, int(moved // 4) // 8 * 8)  # bf16 elements of one buffer (read + write = moved)
+            bufs = [torch.zeros(elems, dtype=torch.bfloat16, device=dev) for _ in range(64)]
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                for b in bufs:
+                    b.add_(1.0)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    for b in bufs:
+                        b.add_(1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            ea.record()
+            for _ in range(reps):
+                g.replay()
+            eb.record()
+            torch.cuda.synchronize()
+            us = 1e3 * ea.elapsed_time(eb) / (reps * len(bufs))
+            legs[kind] = {"bytes": 4 * elems, "avg_us": us, "GBps": 4 * elems / (us * 1e-6) / 1e9,
+                          "frac": 4 * elems / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "kernel_vs_reference": avg_us[kind] / us}
+            del bufs, g
+        torch.cuda.empty_cache()
+        stream_ref["launch_sized_inplace_add"] = legs
+        log("launch-sized in-place add: " + " ".join(f"{k}: {v['bytes'] / 1e6:.2f} MB {v['avg_us']:.2f}us "
+                                                      f"({v['frac']:.3f}; call/ref {v['kernel_vs_reference']:.2f})"
+                                                      for k, v in legs.items()))
         log(f"reference streams: in-place add {stream_ref['inplace_add_GBps']:.0f} GB/s, "
             f"row max read {stream_ref['row_max_read_GBps']:.0f} GB/s")
 
@@ -608,7 +702,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "host_routing_us_per_step": 1e6 * host_route_s[0] / args.steps,
+        "host_routing_us_per_step": 1e6 * ctx["host_route_s"] / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -621,16 +715,19 @@ def main():
                    "max_lora_rank": R, "layers_per_step": n_layers, "path": args.path,
                    "api": args.api, "routing": "device" if args.device_routing else "host+device",
                    "token_routing": bool(args.token_routing),
-                   "hip_graph": graph is not None, "lora_bias": bool(args.bias)},
+                   "hip_graph": not args.no_graph, "lora_bias": bool(args.bias)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
                      "algorithmic_bytes_per_launch": kbytes[dominant],
                      "avg_launch_us": avg_us[dominant]},
         "calls": {k: {"avg_us": avg_us[k], "bytes": kbytes[k], "flops": kflops[k],
-                      "GBps": kbytes[k] / (avg_us[k] * 1e-6) / 1e9} for k in KINDS},
+                      "GBps": kbytes[k] / (avg_us[k] * 1e-6) / 1e9,
+                      "frac": kbytes[k] / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS} for k in KINDS},
+        "calls_per_timed_graph": ctx["graph_calls"],
+        "prefill": prefill,
         "end_to_end_GBps": e2e_gbs,
         "stream_reference": stream_ref,
-        "pack_ms_per_adapter_layer": 1e3 * t_pack / max(n_pack, 1),
+        "pack_ms_per_adapter_layer": 1e3 * ctx["t_pack"] / max(ctx["n_pack"], 1),
         "activation": activation,
         "cpu_baseline": cpu,
     }

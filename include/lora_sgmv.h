@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 8
+#define LORA_ABI_VERSION 9
 
 /* Status codes, modelled on the page's LoRAStatus enum ([MAX-lora] LoRAStatus
  * table: SUCCESS, LOAD_INVALID_ADAPTER, UNSPECIFIED_ERROR, ...) and on the
@@ -362,6 +362,13 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  * which kernels compute it (and so the fp32 summation order); a NULL pointer
  * means the library's defaults, which are the measured best.  A negative
  * value (0 for fused_feature_tile) selects the default of that field.
+ *   long_delta          AUTO on a batch with longer groups: the one-kernel
+ *                       delta for long groups (workgroups of at most 64
+ *                       tokens doing the shrink and the expand; bf16, ranks
+ *                       16 to 64 with n_slices*R <= 64, slice widths
+ *                       multiples of 64, host routing copy): -1 when the
+ *                       batch fills the chip without splitting K (prefill-
+ *                       sized batches), 0 never, 1 whenever it applies.
  *   fused_max_tokens    AUTO takes the one-kernel path when no group has more
  *                       tokens than this (default 32; 0: never).
  *   splitk_short        on that path, the split-K form for an input width
@@ -376,6 +383,7 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  *                       sums in a separate pass before the expand: -1 from
  *                       2048 LoRA-routed tokens, 0 never, 1 always. */
 typedef struct lora_options {
+    int32_t long_delta;
     int32_t fused_max_tokens;
     int32_t splitk_short;
     int32_t fused_feature_tile;
@@ -397,10 +405,11 @@ typedef struct lora_options {
  * are neither read nor written.  Arguments as for lora_sgmv_shrink and
  * lora_sgmv_expand (bias_stack as there); workspace >= lora_sgmv_workspace_bytes(dims, family, end)
  * bytes, 16-byte aligned; it must not alias x, y or the stacks.
- * path: any LORA_PATH_*; with the one-kernel path (FUSED, or AUTO on short
- * groups when the split-K form above is not taken) the workspace is not
- * touched and may be NULL (AUTO then never takes the split-K form), and y
- * must not alias x or the stacks.  On the other paths a NULL workspace is
+ * path: any LORA_PATH_*; with the one-kernel paths (FUSED, or AUTO on short
+ * groups when the split-K form above is not taken, or AUTO's one-kernel
+ * delta for long groups, see lora_options_t) the workspace is not touched
+ * and may be NULL (AUTO then never takes the split-K form), and y must not
+ * alias x or the stacks.  On the other paths a NULL workspace is
  * LORA_ERR_INVALID_ARGUMENT and a short one LORA_ERR_CAPACITY.
  * options: NULL or the tuning choices above.
  */

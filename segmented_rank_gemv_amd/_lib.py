@@ -52,7 +52,7 @@ MAX_HOST_GROUPS = 64
 
 
 class _LoraOptions(ctypes.Structure):
-    _fields_ = [("fused_max_tokens", ctypes.c_int32), ("splitk_short", ctypes.c_int32),
+    _fields_ = [("long_delta", ctypes.c_int32), ("fused_max_tokens", ctypes.c_int32), ("splitk_short", ctypes.c_int32),
                 ("fused_feature_tile", ctypes.c_int32), ("fused_k_rotation", ctypes.c_int32),
                 ("fold_slabs", ctypes.c_int32)]
 
@@ -62,6 +62,7 @@ class LoraOptions:
     """Tuning choices of lora_sgmv_delta (lora_options_t).  -1 (0 for
     fused_feature_tile) keeps the library default; none changes what is
     computed, only which kernels compute it."""
+    long_delta: int = -1
     fused_max_tokens: int = -1
     splitk_short: int = -1
     fused_feature_tile: int = 0
@@ -69,8 +70,8 @@ class LoraOptions:
     fold_slabs: int = -1
 
     def c(self) -> _LoraOptions:
-        return _LoraOptions(self.fused_max_tokens, self.splitk_short, self.fused_feature_tile,
-                            self.fused_k_rotation, self.fold_slabs)
+        return _LoraOptions(self.long_delta, self.fused_max_tokens, self.splitk_short,
+                            self.fused_feature_tile, self.fused_k_rotation, self.fold_slabs)
 
 
 class LoraRouting:

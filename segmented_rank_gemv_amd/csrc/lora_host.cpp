@@ -110,6 +110,19 @@ ShrinkPlan plan_shrink(const FamilyShape& fs, int64_t end, int groups)
 
 size_t shrink_workspace(const ShrinkPlan& p) { return p.S > 1 ? (size_t)p.S * p.slab_bytes : 0; }
 
+LongPlan plan_long(const FamilyShape& fs, int64_t tiles)
+{
+    LongPlan p;
+    p.nz = (fs.C + kLongCols - 1) / kLongCols;
+    p.cb = ((fs.C + p.nz - 1) / p.nz + 15) / 16 * 16;
+    const int64_t units = (fs.in_f + kLongKUnit - 1) / kLongKUnit;
+    int64_t S = kPlanCUs / std::max<int64_t>(1, tiles * p.nz);
+    S = std::min(std::max<int64_t>(S, 1), units);
+    p.kc = (int)((units + S - 1) / S) * kLongKUnit;
+    p.S = (fs.in_f + p.kc - 1) / p.kc;
+    return p;
+}
+
 size_t delta_workspace(const ShrinkPlan& p) { return (size_t)p.S * p.slab_bytes; }
 
 size_t workspace_bound(const FamilyShape& fs, int64_t max_tokens)
@@ -131,6 +144,19 @@ size_t workspace_bound(const FamilyShape& fs, int64_t max_tokens)
         ShrinkPlan p = plan_from_tiles(fs, (int)std::min<int64_t>(most + 1, 1 << 30), max_tokens);
         best = std::max(best, delta_workspace(p));
     }
+    // the long-segment kernel: a batch of `end` tokens has at least
+    // ceil(end / kLongRows) tiles of kLongRows, and S only grows as the tile
+    // count shrinks; every call keeps u (S slabs) in the workspace at most
+    const size_t row = (size_t)fs.C * sizeof(float);
+    const int64_t lmost = (max_tokens + kLongRows - 1) / kLongRows;
+    for (int64_t k = 1; k <= lmost; ++k) {
+        const int64_t e = std::min<int64_t>(k * kLongRows, max_tokens);
+        const LongPlan p = plan_long(fs, k);
+        best = std::max(best, (size_t)p.S * (size_t)e * row);
+        if (p.S == 1)
+            break;
+    }
+    best = std::max(best, (size_t)plan_long(fs, lmost).S * (size_t)max_tokens * row);
     return best;
 }
 

@@ -71,6 +71,23 @@ struct ShrinkPlan {
 
 // Plan for a given number of routed tokens and groups.
 ShrinkPlan plan_shrink(const FamilyShape& fs, int64_t end, int groups);
+
+// Plan of the long-segment shrink (bf16): column groups of at most 64
+// columns, and K split S ways in ranges of kc (a multiple of kLongKUnit)
+// so that a batch of `tiles` 64-token tiles fills about kPlanCUs workgroups.
+// (kPlanCUs is MI355X's compute-unit count, a constant so that the
+// workspace bound does not depend on the device.)
+constexpr int kLongRows = 64;
+constexpr int kLongKUnit = 256;
+constexpr int kLongCols = 64;
+constexpr int kPlanCUs = 256;
+struct LongPlan {
+    int nz;  // column groups
+    int cb;  // columns per group (multiple of 16, <= kLongCols)
+    int S;   // K splits
+    int kc;  // K range of one split
+};
+LongPlan plan_long(const FamilyShape& fs, int64_t tiles);
 // Workspace of lora_sgmv_shrink (slabs only when S > 1).
 size_t shrink_workspace(const ShrinkPlan& p);
 // Workspace of lora_sgmv_delta (always the S slabs).

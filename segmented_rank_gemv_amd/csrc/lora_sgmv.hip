@@ -56,6 +56,7 @@ namespace lora {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;  // consecutive workgroups go to consecutive XCDs
 // K elements one MFMA-shrink workgroup stages per pass (row runs of 2 KC bytes)
 constexpr int kShrinkKC = LORA_SHRINK_KC;
 
@@ -681,6 +682,217 @@ __global__ __launch_bounds__(kThreads) void reduce_slabs(const float* P, int64_t
         acc.w += v.w;
     }
     reinterpret_cast<float4*>(u)[i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// long-segment shrink (bf16, MFMA)
+//
+// One 512-thread workgroup owns a piece of at most 64 consecutive tokens of
+// one group, one group of at most 16 NB columns of u, and one K range
+// [kb, ke) (all of K unless the launch splits K).  Its 8 waves split the K
+// range; wave w streams the piece's 64 rows of x over its K share, and the
+// matching A rows, straight into registers, P 32-element steps ahead of the
+// matrix instructions, with no LDS and no barrier in the loop.  Per step the
+// wave issues four x loads (16 rows x 64 bytes each, the M operands of the
+// four 16-row blocks) and NB A loads (16 columns x 32 K values each, one
+// contiguous 1 KB run of the tiled layout: the N operands), then 4 NB
+// v_mfma_f32_16x16x32_bf16.  K positions past the range and rows past the
+// piece read zero through the buffer bounds.  The 8 partial tiles are then
+// added in LDS in a fixed tree order ((w0 + w4) + (w2 + w6)) + ((w1 + w5) +
+// (w3 + w7)), so the result is deterministic, and written to u, or to slab s
+// of the workspace when K is split.
+//
+// Pieces: each group is cut into n_g near-equal pieces of at most 64 tokens;
+// n_g is raised above ceil(len / 64) while that still leaves one workgroup
+// per compute unit, so a batch of a few long groups spreads over the whole
+// chip.  Workgroup b runs on XCD b % 8 and the pieces are dealt to the XCDs
+// in contiguous runs, so a group's A rows are fetched into few L2s.
+constexpr int kLsWaves = 8;
+constexpr int kLsThreads = 64 * kLsWaves;
+constexpr int kLsRows = 64;               // tokens of a piece: four 16-row MFMA blocks
+constexpr int kLsKUnit = 32 * kLsWaves;   // K split granularity: one step of every wave
+
+struct LongShrinkArgs {
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* A;  // [L][a_slot] in the tiled A layout
+    int64_t a_slot;
+    float* out;         // u (S == 1) or slab s at out + s * slab, each [end][C]
+    int64_t slab;
+    int in_f, C;
+    int kc;       // K range of one split (a multiple of kLsKUnit)
+    int zs;       // column groups x K splits
+    int S;        // K splits
+    int cb;       // columns per column group (a multiple of 16)
+    int per_xcd;  // pieces dealt to each XCD
+    int pieces;   // pieces in total
+    RouteArgs r;
+    int k_piece0[LORA_MAX_HOST_GROUPS + 1];  // host routing: first piece of each group
+};
+
+// The piece: with the host copy of the routing, group g holds pieces
+// [k_piece0[g], k_piece0[g + 1]) of near-equal length; without it, 64-token
+// tiles found by a scan over the device arrays.
+__device__ __forceinline__ bool locate_piece(const LongShrinkArgs& a, int piece, TileInfo& ti)
+{
+    if (!a.r.kr)
+        return locate_tile<kLsRows, false>(a.r, piece, ti);
+    const int lane = threadIdx.x & 63;
+    const bool in = lane < a.r.G;
+    const int p0_l = in ? a.k_piece0[lane] : 0;
+    const int p1_l = in ? a.k_piece0[lane + 1] : 0;
+    const int gs_l = in ? a.r.k_offs[lane] : 0;
+    const int ge_l = in ? a.r.k_offs[lane + 1] : 0;
+    const int id_l = in ? a.r.k_ids[lane] : -1;
+    const unsigned long long hit = __ballot(in && piece < p1_l);
+    if (!hit)
+        return false;
+    const int g = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+    const int p0 = __builtin_amdgcn_readlane(p0_l, g), np = __builtin_amdgcn_readlane(p1_l, g) - p0;
+    const int gs = __builtin_amdgcn_readlane(gs_l, g), len = __builtin_amdgcn_readlane(ge_l, g) - gs;
+    const int j = piece - p0;
+    const int t0 = gs + (int)(((int64_t)len * j) / np);
+    const int t1 = gs + (int)(((int64_t)len * (j + 1)) / np);
+    ti.g = g;
+    ti.t0 = t0;
+    ti.n = t1 - t0;
+    ti.glen = len;
+    ti.slot = __builtin_amdgcn_readlane(id_l, g);
+    return ti.slot >= 0 && ti.slot < a.r.L;
+}
+
+template <int NB>
+struct LongShrinkLds {
+    static constexpr int kLd = 16 * NB + 4;          // padded row of a partial tile (floats)
+    static constexpr int kTile = kLsRows * kLd;      // one wave's partial tile
+    static constexpr int kFloats = 4 * kTile;        // four tiles in flight in the tree
+};
+
+template <int NB, int P, bool GATHER>
+__global__ __launch_bounds__(kLsThreads) void shrink_long_kernel(LongShrinkArgs a)
+{
+    typedef LongShrinkLds<NB> Lay;
+    __shared__ __attribute__((aligned(16))) float red[Lay::kFloats];
+    asm volatile("" ::"s"(a.x), "s"(a.ldx), "s"(a.A), "s"(a.a_slot), "s"(a.out), "s"(a.slab), "s"(a.in_f),
+                 "s"(a.C), "s"(a.kc), "s"(a.zs), "s"(a.S), "s"(a.cb), "s"(a.per_xcd), "s"(a.pieces), "s"(a.r.G),
+                 "s"(a.r.kr));
+    const int b = blockIdx.x;
+    const int i = b / kXcds;
+    const int zsi = i % a.zs;
+    const int piece = (b % kXcds) * a.per_xcd + i / a.zs;
+    if (piece >= a.pieces)
+        return;
+    TileInfo ti;
+    if (!locate_piece(a, piece, ti))
+        return;
+    const int z = zsi / a.S, s = zsi - z * a.S;
+    const int c0 = z * a.cb, cw = min(a.cb, a.C - c0);
+    const int kb = s * a.kc, ke = min(kb + a.kc, a.in_f);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int kw = a.kc / kLsWaves;
+    const int k0 = kb + w * kw, k1 = min(k0 + kw, ke);
+    const int nsteps = k1 > k0 ? (k1 - k0 + 31) >> 5 : 0;
+
+    const RowMap<GATHER> xm{a.r.rows, ti.t0, ti.n, a.r.nrows};
+    const Buf xb = xm.buf(a.x, a.ldx);
+    uint32_t xrow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        xrow[m] = (uint32_t)(xm(16 * m + l16) * a.ldx) * 2;
+    const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)(c0 >> 4) * 16 * a.in_f,
+                 (uint32_t)(((cw + 15) >> 4) * 16 * a.in_f * 2));
+    const uint32_t ablk = (uint32_t)(16 * a.in_f) * 2;
+
+    uint4 xr[P][4], ar[P][NB];
+    f32x4_t acc[4][NB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto load = [&](int st, uint4(&xv)[4], uint4(&av)[NB]) {
+        const int kk = k0 + 32 * st + 8 * q;
+        const bool ok = kk < k1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            xv[m] = xb.ld16(ok ? xrow[m] + (uint32_t)kk * 2 : kOOB);
+        const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 16);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            av[nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+    };
+    // the prologue issues the steps in slot order too, so that at the loop
+    // head slot j's loads are as old along both incoming edges
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        load(j, xr[j], ar[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int base = 0; base < nsteps; base += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[j][m]),
+                                                                        __builtin_bit_cast(bf16x8_t, ar[j][nb]),
+                                                                        acc[m][nb], 0, 0, 0);
+            load(base + P + j, xr[j], ar[j]);
+            // keep each step's reload right after its matrix instructions:
+            // left alone, the scheduler sinks every reload to the end of the
+            // body and the loop head then waits for all of them
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // D of block (m, nb): lane holds column 16 nb + l16 of rows 16 m + 4 q + r
+    auto put = [&](int t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    red[t * Lay::kTile + (16 * m + 4 * q + r) * Lay::kLd + 16 * nb + l16] = acc[m][nb][r];
+    };
+    auto add = [&](int t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][nb][r] += red[t * Lay::kTile + (16 * m + 4 * q + r) * Lay::kLd + 16 * nb + l16];
+    };
+    if (w >= 4)
+        put(w - 4);
+    __syncthreads();
+    if (w < 4)
+        add(w);
+    __syncthreads();
+    if (w == 2 || w == 3)
+        put(w - 2);
+    __syncthreads();
+    if (w < 2)
+        add(w);
+    __syncthreads();
+    if (w == 1)
+        put(0);
+    __syncthreads();
+    if (w == 0) {
+        add(0);
+        put(0);
+    }
+    __syncthreads();
+    // rows [0, n) x columns [0, cw) of the sum, four floats per thread
+    float* dst = a.out + (size_t)s * a.slab + (size_t)ti.t0 * a.C + c0;
+    const int c4 = cw >> 2;
+    for (int e = tid; e < ti.n * c4; e += kLsThreads) {
+        const int row = e / c4, c = e - row * c4;
+        *reinterpret_cast<float4*>(dst + (size_t)row * a.C + 4 * c) =
+            *reinterpret_cast<const float4*>(red + row * Lay::kLd + 4 * c);
+    }
 }
 
 // Zero n 16-byte words (slot reset; a kernel rather than a memset so that
@@ -1318,6 +1530,325 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// one-kernel delta for long groups (prefill-sized batches; bf16, C <= 64)
+//
+// One 512-thread workgroup owns a piece of at most 64 consecutive tokens of
+// one group (the long shrink's pieces: about one workgroup per compute unit)
+// and computes its whole delta, so u never leaves the chip and the family
+// takes one launch.
+//
+// Phase 1 (shrink): the 8 waves split K.  A wave moves x in chunks of 64 K
+// values: eight loads of whole 128-byte lines (8 rows x 128 B each; the
+// matrix layout would split every line over two loads, which measured about
+// 20 % slower on this part) into registers, then into its own 8 KB LDS
+// region (16-byte pieces rotated by row, so that both the line writes and
+// the fragment reads spread over the banks), from which it reads the
+// v_mfma_f32_16x16x32_bf16 M operands of its 64 rows.  A fragments come
+// straight from the tiled layout (one contiguous 1 KB run each).  Loads run
+// D chunks ahead.  The 8 partial tiles are added in LDS in the long shrink's
+// fixed tree order; u [64][C] (fp32) stays in LDS.
+//
+// Phase 2 (expand): the waves split the output features in runs of 64.  For
+// each run a wave loads the piece's 64 rows x 128 B of y as whole lines,
+// rotates them through its LDS region into the MFMA C layout (lane = token,
+// 8 consecutive features), adds B.u (B rows as the M operand, u = hi + lo
+// bf16 halves as the N operand, as in the other expand kernels) and the
+// bias, writes the rounded result back in place, and stores it as whole
+// lines.  All accesses of x and y go through buffer bounds: rows past the
+// piece read zero and drop their stores.
+constexpr int kLdWaveBytes = 64 * 128;  // a wave's LDS region: 64 rows x 128 B
+
+struct LongDeltaArgs {
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* A;  // [L][a_slot] in the tiled A layout
+    int64_t a_slot;
+    const uint16_t* B;     // [L][out_f][R]
+    const uint16_t* bias;  // [L][out_f] or null
+    uint16_t* y;
+    int64_t ldy;
+    int in_f, C, out_f, n_s;
+    int soff[5];
+    int kw;  // K range of one wave (a multiple of 32)
+    int fw;  // output features of one wave (a multiple of 64)
+    int per_xcd, pieces;
+    RouteArgs r;
+    int k_piece0[LORA_MAX_HOST_GROUPS + 1];
+};
+
+template <int NB, int NH>
+struct LongDeltaLds {
+    static constexpr int kRegions = kLsWaves * kLdWaveBytes;
+    static constexpr int kRed = LongShrinkLds<NB>::kFloats * 4;
+    static constexpr int kU = (kRegions > kRed ? kRegions : kRed);  // offset of u [64][16 NB] fp32
+    static constexpr int kBytes = kU + kLsRows * 16 * NB * 4;
+};
+
+// byte offset in a wave's region of 16-byte piece p (0..7) of row r
+__device__ __forceinline__ int ld_slot(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
+
+template <int NB, int NH, int D, int D2, bool GATHER>
+__global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
+{
+    typedef LongDeltaLds<NB, NH> Lay;
+    constexpr int R = 16 * NH;
+    __shared__ __attribute__((aligned(16))) char smem[Lay::kBytes];
+    asm volatile("" ::"s"(a.x), "s"(a.ldx), "s"(a.A), "s"(a.a_slot), "s"(a.B), "s"(a.bias), "s"(a.y), "s"(a.ldy),
+                 "s"(a.in_f), "s"(a.C), "s"(a.out_f), "s"(a.kw), "s"(a.fw), "s"(a.per_xcd), "s"(a.pieces),
+                 "s"(a.r.G), "s"(a.r.kr));
+    const int b = blockIdx.x;
+    const int piece = (b % kXcds) * a.per_xcd + b / kXcds;
+    if (piece >= a.pieces)
+        return;
+    TileInfo ti;
+    {
+        // the long shrink's pieces (locate_piece)
+        if (!a.r.kr) {
+            if (!locate_tile<kLsRows, false>(a.r, piece, ti))
+                return;
+        } else {
+            const int lane = threadIdx.x & 63;
+            const bool in = lane < a.r.G;
+            const int p0_l = in ? a.k_piece0[lane] : 0;
+            const int p1_l = in ? a.k_piece0[lane + 1] : 0;
+            const int gs_l = in ? a.r.k_offs[lane] : 0;
+            const int ge_l = in ? a.r.k_offs[lane + 1] : 0;
+            const int id_l = in ? a.r.k_ids[lane] : -1;
+            const unsigned long long hit = __ballot(in && piece < p1_l);
+            if (!hit)
+                return;
+            const int g = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+            const int p0 = __builtin_amdgcn_readlane(p0_l, g), np = __builtin_amdgcn_readlane(p1_l, g) - p0;
+            const int gs = __builtin_amdgcn_readlane(gs_l, g), len = __builtin_amdgcn_readlane(ge_l, g) - gs;
+            const int j = piece - p0;
+            ti.t0 = gs + (int)(((int64_t)len * j) / np);
+            ti.n = gs + (int)(((int64_t)len * (j + 1)) / np) - ti.t0;
+            ti.slot = __builtin_amdgcn_readlane(id_l, g);
+            if (ti.slot < 0 || ti.slot >= a.r.L)
+                return;
+        }
+    }
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int lr = lane >> 3, lp = lane & 7;  // whole-line layout: row lr + 8 i, 16-byte piece lp
+    char* region = smem + w * kLdWaveBytes;
+    const RowMap<GATHER> rm{a.r.rows, ti.t0, ti.n, a.r.nrows};
+
+    // ---------------- phase 1: u = A . x over the wave's K range
+    const Buf xb = rm.buf(a.x, a.ldx);
+    uint32_t xro[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        xro[i] = (uint32_t)(rm(lr + 8 * i) * a.ldx) * 2;
+    const Buf ab(a.A + (size_t)ti.slot * a.a_slot, (uint32_t)(NB * 16 * a.in_f * 2));
+    const uint32_t ablk = (uint32_t)(16 * a.in_f) * 2;
+    const int k0 = w * a.kw, k1 = min(k0 + a.kw, a.in_f);
+    const int nch = k1 > k0 ? (k1 - k0 + 63) >> 6 : 0;
+    f32x4_t acc[4][NB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 xs[D][8], as[D][2][NB];
+    auto load_x = [&](int ch, uint4(&xv)[8], uint4(&av)[2][NB]) {
+        const int kx = k0 + 64 * ch + 8 * lp;
+        const bool okx = kx < k1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            xv[i] = xb.ld16(okx ? xro[i] + (uint32_t)kx * 2 : kOOB);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int kk = k0 + 64 * ch + 32 * s + 8 * q;
+            const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 16);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                av[s][nb] = ab.ld16(kk < k1 ? nb * ablk + ao : kOOB);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        load_x(j, xs[j], as[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int base = 0; base < nch; base += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            // whole lines into the wave's region, then the M operands out of it
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint4*>(region + ld_slot(lr + 8 * i, lp)) = xs[j][i];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 xf = *reinterpret_cast<const uint4*>(region + ld_slot(16 * m + l16, 4 * s + q));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xf), __builtin_bit_cast(bf16x8_t, as[j][s][nb]), acc[m][nb],
+                            0, 0, 0);
+                }
+            load_x(base + D + j, xs[j], as[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // partial tiles -> LDS tree (fixed order) -> u [64][16 NB] in LDS
+    float* red = reinterpret_cast<float*>(smem);
+    float* us = reinterpret_cast<float*>(smem + Lay::kU);
+    constexpr int kLd = LongShrinkLds<NB>::kLd, kTile = LongShrinkLds<NB>::kTile;
+    auto put = [&](int t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    red[t * kTile + (16 * m + 4 * q + r) * kLd + 16 * nb + l16] = acc[m][nb][r];
+    };
+    auto add = [&](int t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][nb][r] += red[t * kTile + (16 * m + 4 * q + r) * kLd + 16 * nb + l16];
+    };
+    __syncthreads();  // every wave is done with its region before the tree reuses it
+    if (w >= 4)
+        put(w - 4);
+    __syncthreads();
+    if (w < 4)
+        add(w);
+    __syncthreads();
+    if (w == 2 || w == 3)
+        put(w - 2);
+    __syncthreads();
+    if (w < 2)
+        add(w);
+    __syncthreads();
+    if (w == 1)
+        put(0);
+    __syncthreads();
+    if (w == 0) {
+        add(0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    us[(16 * m + 4 * q + r) * (16 * NB) + 16 * nb + l16] = acc[m][nb][r];
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: y += B . u (+ bias) over the wave's features
+    const Buf yb = rm.buf(a.y, a.ldy);
+    uint32_t yro[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        yro[i] = (uint32_t)(rm(lr + 8 * i) * a.ldy) * 2;
+    const Buf bb(a.B + (size_t)ti.slot * a.out_f * R, (uint32_t)(a.out_f * R * 2));
+    const Buf biasb(a.bias + (size_t)ti.slot * a.out_f, a.bias ? (uint32_t)(a.out_f * 2) : 0u);
+    const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0 (see expand_mfma)
+    const int fb = w * a.fw, fe = min(fb + a.fw, a.out_f);
+    const int ntl = fe > fb ? (fe - fb) >> 6 : 0;
+    uint4 ys[D2][8], bs[D2][2][2][NH], bis[D2][2];
+    auto load_y = [&](int t, uint4(&yv)[8], uint4(&bv)[2][2][NH], uint4(&biv)[2]) {
+        const int f = fb + 64 * t;
+        const bool ok = t < ntl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            yv[i] = yb.ld16(ok ? yro[i] + (uint32_t)(f + 8 * lp) * 2 : kOOB);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int kh = 0; kh < NH; ++kh)
+                    bv[h][hh][kh] =
+                        bb.ld16(ok ? (uint32_t)((f + 32 * h + mrow + 4 * hh) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+            biv[h] = biasb.ld16(ok ? (uint32_t)(f + 32 * h + 8 * q) * 2 : kOOB);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < D2; ++j) {
+        load_y(j, ys[j], bs[j], bis[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int cur_sl = -1;
+    bf16x8_t uf[4][NH];
+    for (int base = 0; base < ntl; base += D2) {
+#pragma unroll
+        for (int j = 0; j < D2; ++j) {
+            const int t = base + j;
+            if (t < ntl) {
+                const int f = fb + 64 * t;
+                int sl = 0;
+#pragma unroll
+                for (int i = 1; i < 4; ++i)
+                    if (i < a.n_s && f >= a.soff[i])
+                        sl = i;
+                if (sl != cur_sl) {
+                    // u fragments of the slice: lanes q < 2 carry hi(u), q >= 2 lo(u)
+                    cur_sl = sl;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int kh = 0; kh < NH; ++kh) {
+                            const float* up = us + (16 * m + l16) * (16 * NB) + sl * R + 16 * kh + 8 * (q & 1);
+                            uint32_t pk[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float v0 = up[2 * e], v1 = up[2 * e + 1];
+                                uint32_t hi = f2bf_pair(v0, v1);
+                                if (q >= 2)
+                                    hi = f2bf_pair(v0 - bf2f(hi & 0xFFFFu), v1 - bf2f(hi >> 16));
+                                pk[e] = hi;
+                            }
+                            uf[m][kh] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                        }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint4*>(region + ld_slot(lr + 8 * i, lp)) = ys[j][i];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        uint4* cell = reinterpret_cast<uint4*>(region + ld_slot(16 * m + l16, 4 * h + q));
+                        const uint4 yv = *cell;
+                        f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
+                        f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
+                        if (a.bias)
+                            add_bias8(bis[j][h], acc0, acc1);
+#pragma unroll
+                        for (int kh = 0; kh < NH; ++kh) {
+                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bs[j][h][0][kh]),
+                                                                          uf[m][kh], acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bs[j][h][1][kh]),
+                                                                          uf[m][kh], acc1, 0, 0, 0);
+                        }
+                        uint4 o;
+                        o.x = f2bf_pair(acc0[0], acc0[1]);
+                        o.y = f2bf_pair(acc0[2], acc0[3]);
+                        o.z = f2bf_pair(acc1[0], acc1[1]);
+                        o.w = f2bf_pair(acc1[2], acc1[3]);
+                        *cell = o;
+                    }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    yb.st16(yro[i] + (uint32_t)(f + 8 * lp) * 2,
+                            *reinterpret_cast<const uint4*>(region + ld_slot(lr + 8 * i, lp)));
+            }
+            load_y(base + D2 + j, ys[j], bs[j], bis[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // one-kernel delta for short groups (decode batches)
 //
 // A decode batch moves a few MB per family, so a launch and a round trip to
@@ -1338,7 +1869,6 @@ constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kFusedTileM = 16;
 constexpr int kFusedMaxFeat = 32 * kFusedWaves;  // one 32-feature pair per wave
-constexpr int kXcds = 8;
 
 // A token tile as the host lays it out from its copy of the routing (the
 // same tiles locate_tile<kFusedTileM, true> finds).
@@ -1834,6 +2364,7 @@ int pick_mode(int path, bool mfma_ok, int valu_max, const RouteArgs& r)
 
 // The caller's tuning choices (lora_options_t), resolved to values.
 struct Tuning {
+    int long_delta;    // -1 auto, 0 never, 1 whenever it applies
     int fused_max;     // longest group for which AUTO takes the one-kernel delta
     int splitk_short;  // -1 auto, 0 never, 1 whenever it applies
     int feat;          // one-kernel feature tile cap (0: automatic)
@@ -1850,6 +2381,7 @@ constexpr int kDeltaFoldTokens = 2048;
 
 lora_status_t resolve_options(const lora_options_t* o, Tuning* t)
 {
+    t->long_delta = -1;
     t->fused_max = kFusedMaxTokens;
     t->splitk_short = -1;
     t->feat = 0;
@@ -1869,6 +2401,7 @@ lora_status_t resolve_options(const lora_options_t* o, Tuning* t)
     if (o->fused_k_rotation >= 0)
         t->krot = o->fused_k_rotation > 0;
     t->fold = o->fold_slabs < 0 ? -1 : o->fold_slabs > 0;
+    t->long_delta = o->long_delta < 0 ? -1 : o->long_delta > 0;
     return LORA_OK;
 }
 
@@ -1973,6 +2506,125 @@ lora_status_t run_shrink(const Common& c, const ShrinkPlan& plan, const void* x,
     const int mode = pick_mode(path, shrink_mfma_ok(c), a.valu_max, c.r);
     const hipError_t e = launch_shrink(c.bf16, mode, a, plan.cb / 16, (int)grid, s);
     return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
+// Which shrink kernel a call runs, with its launch plan.  The long-segment
+// kernel takes every bf16 call that does not force the VALU path.
+struct ShrinkChoice {
+    bool lng;
+    ShrinkPlan old;  // the 256-thread kernel's plan (lng false)
+    LongPlan lp;     // the long-segment kernel's plan (lng true)
+    int pieces, per_xcd;
+    int k_piece0[LORA_MAX_HOST_GROUPS + 1];
+    int S() const { return lng ? lp.S : old.S; }
+    size_t slab_bytes(const Common& c) const { return (size_t)c.r.end * c.fs.C * sizeof(float); }
+};
+
+// 64-token tiles of the batch: exact with the host copy of the routing,
+// else a bound.
+int64_t long_tiles(const Common& c)
+{
+    if (!c.r.kr)
+        return ((int64_t)c.r.end + kLongRows - 1) / kLongRows + c.r.G;
+    int64_t t = 0;
+    for (int g = 0; g < c.r.G; ++g)
+        t += (c.r.k_offs[g + 1] - c.r.k_offs[g] + kLongRows - 1) / kLongRows;
+    return t;
+}
+
+ShrinkChoice choose_shrink(const Common& c, int32_t path)
+{
+    ShrinkChoice ch;
+    const int64_t tiles = long_tiles(c);
+    ch.lp = plan_long(c.fs, tiles);
+    // the long-segment kernel only where its plan splits no K (batches that
+    // fill the chip with 64-token pieces): with a K split, the 256-thread
+    // kernel measured faster (32-layer stack shrink_qkv 22.0 against 23.6 us,
+    // mixed batch 24.2 against 30.0 us)
+    ch.lng = shrink_mfma_ok(c) && path != LORA_PATH_VALU && ch.lp.S == 1;
+    if (!ch.lng)
+        ch.old = plan_shrink(c.fs, c.r.end, c.r.G);
+    // the pieces of the long-segment kernels (the long delta may be forced
+    // where the long shrink is not taken)
+    if (!c.r.kr) {
+        ch.pieces = (int)tiles;
+    } else {
+        // more, shorter pieces while that still leaves about one workgroup
+        // per compute unit (only when K is not split)
+        const int64_t end = std::max<int64_t>(c.r.end, 1);
+        ch.k_piece0[0] = 0;
+        for (int g = 0; g < c.r.G; ++g) {
+            const int64_t len = c.r.k_offs[g + 1] - c.r.k_offs[g];
+            int64_t n = (len + kLongRows - 1) / kLongRows;
+            if (ch.lp.S == 1)
+                n = std::max<int64_t>(n, len * kPlanCUs / (end * ch.lp.nz));
+            ch.k_piece0[g + 1] = ch.k_piece0[g] + (int)n;
+        }
+        ch.pieces = ch.k_piece0[c.r.G];
+    }
+    ch.per_xcd = (ch.pieces + kXcds - 1) / kXcds;
+    return ch;
+}
+
+// Workspace a shrink choice needs: the S > 1 slabs (lora_sgmv_shrink), or
+// u itself as well (lora_sgmv_delta keeps u in the workspace).
+size_t shrink_need(const Common& c, const ShrinkChoice& ch, bool delta)
+{
+    const int S = ch.S();
+    return (delta || S > 1) ? (size_t)S * ch.slab_bytes(c) : 0;
+}
+
+template <bool G>
+hipError_t launch_shrink_long(const LongShrinkArgs& a, int nb, dim3 grid, hipStream_t st)
+{
+    switch (nb) {
+    case 1: hipLaunchKernelGGL((shrink_long_kernel<1, 8, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_long_kernel<2, 6, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((shrink_long_kernel<3, 4, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_long_kernel<4, 4, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+lora_status_t run_shrink_long(const Common& c, const ShrinkChoice& ch, const void* x, int64_t ldx,
+                              const void* A_stack, float* out, hipStream_t s)
+{
+    LongShrinkArgs a;
+    a.x = reinterpret_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.A = reinterpret_cast<const uint16_t*>(A_stack);
+    a.a_slot = a_tiled_elems(c.fs.C, c.fs.in_f);
+    a.out = out;
+    a.slab = (int64_t)c.r.end * c.fs.C;
+    a.in_f = c.fs.in_f;
+    a.C = c.fs.C;
+    a.kc = ch.lp.kc;
+    a.S = ch.lp.S;
+    a.zs = ch.lp.nz * ch.lp.S;
+    a.cb = ch.lp.cb;
+    a.per_xcd = ch.per_xcd;
+    a.pieces = ch.pieces;
+    a.r = c.r;
+    for (int g = 0; g <= LORA_MAX_HOST_GROUPS; ++g)
+        a.k_piece0[g] = c.r.kr && g <= c.r.G ? ch.k_piece0[g] : 0;
+    const int64_t grid = (int64_t)kXcds * ch.per_xcd * a.zs;
+    if (grid > 2147483647LL)
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (grid == 0)
+        return LORA_OK;
+    const int nb = ch.lp.cb / 16;
+    const hipError_t e = c.r.rows ? launch_shrink_long<true>(a, nb, dim3((unsigned)grid), s)
+                                  : launch_shrink_long<false>(a, nb, dim3((unsigned)grid), s);
+    return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
+// The chosen shrink kernel; `out` receives u (S == 1) or the S slabs.
+lora_status_t run_shrink_any(const Common& c, const ShrinkChoice& ch, const void* x, int64_t ldx,
+                             const void* A_stack, float* out, int32_t path, hipStream_t s)
+{
+    if (ch.lng)
+        return run_shrink_long(c, ch, x, ldx, A_stack, out, s);
+    return run_shrink(c, ch.old, x, ldx, A_stack, out, path, s);
 }
 
 bool nh_possible(const Common& c, const ExpandArgs& a) { return expand_mfma_ok(c) && a.valu_max < kTileM; }
@@ -2405,6 +3057,90 @@ bool rows_fit(const Common& c, int64_t ld)
     return !c.r.rows || ((int64_t)c.r.nrows + 1) * ld * c.fs.elem <= (int64_t)kOOB;
 }
 
+// The one-kernel delta for long groups applies to bf16 families whose u has
+// at most 64 columns (ranks 16 to 64), slice widths that are multiples of 64,
+// and a host copy of the routing.
+bool long_delta_ok(const Common& c)
+{
+    bool widths64 = true;
+    for (int sl = 0; sl < c.fs.n_s; ++sl)
+        widths64 = widths64 && c.fs.widths[sl] % 64 == 0;
+    const int R = c.fs.R;
+    return c.bf16 && c.r.kr && widths64 && c.fs.C <= kLongCols && (R == 16 || R == 32 || R == 64);
+}
+
+// AUTO takes it when the batch fills the chip without splitting K (the long
+// shrink's plan has one K split), i.e. on prefill-sized batches; the
+// long_delta option forces it on or off.
+bool long_delta_wanted(const Common& c, const ShrinkChoice& ch)
+{
+    if (!long_delta_ok(c) || c.t.long_delta == 0)
+        return false;
+    return c.t.long_delta > 0 || ch.lng;
+}
+
+template <int NB, int NH>
+void launch_long_delta(bool gather, dim3 grid, hipStream_t s, const LongDeltaArgs& a)
+{
+    constexpr int D = NB <= 2 ? 3 : 2;
+    constexpr int D2 = NH <= 2 ? 2 : 1;
+    if (gather)
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, true>), grid, dim3(kLsThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, false>), grid, dim3(kLsThreads), 0, s, a);
+}
+
+lora_status_t run_long_delta(const Common& c, const ShrinkChoice& ch, const void* x, int64_t ldx,
+                             const void* A_stack, const void* B_stack, const void* bias, void* y, int64_t ldy,
+                             hipStream_t s)
+{
+    LongDeltaArgs a;
+    a.x = reinterpret_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.A = reinterpret_cast<const uint16_t*>(A_stack);
+    a.a_slot = a_tiled_elems(c.fs.C, c.fs.in_f);
+    a.B = reinterpret_cast<const uint16_t*>(B_stack);
+    a.bias = reinterpret_cast<const uint16_t*>(bias);
+    a.y = reinterpret_cast<uint16_t*>(y);
+    a.ldy = ldy;
+    a.in_f = c.fs.in_f;
+    a.C = c.fs.C;
+    a.out_f = c.fs.out_f;
+    a.n_s = c.fs.n_s;
+    for (int i = 0; i < 5; ++i)
+        a.soff[i] = i <= c.fs.n_s ? c.fs.offs[i] : c.fs.out_f;
+    a.kw = (c.fs.in_f + kLsKUnit - 1) / kLsKUnit * 32;
+    a.fw = (c.fs.out_f + 64 * kLsWaves - 1) / (64 * kLsWaves) * 64;
+    a.per_xcd = ch.per_xcd;
+    a.pieces = ch.pieces;
+    a.r = c.r;
+    for (int g = 0; g <= LORA_MAX_HOST_GROUPS; ++g)
+        a.k_piece0[g] = g <= c.r.G ? ch.k_piece0[g] : 0;
+    const int64_t grid = (int64_t)kXcds * ch.per_xcd;
+    if (grid == 0)
+        return LORA_OK;
+    if (grid > 2147483647LL)
+        return LORA_ERR_INVALID_ARGUMENT;
+    const bool gather = c.r.rows != nullptr;
+    const dim3 g((unsigned)grid);
+    const int NH = c.fs.R / 16, NB = c.fs.C / 16;
+    if (NB == 1)
+        launch_long_delta<1, 1>(gather, g, s, a);
+    else if (NB == 2 && NH == 1)
+        launch_long_delta<2, 1>(gather, g, s, a);
+    else if (NB == 3)
+        launch_long_delta<3, 1>(gather, g, s, a);
+    else if (NB == 2)
+        launch_long_delta<2, 2>(gather, g, s, a);
+    else if (NH == 2)
+        launch_long_delta<4, 2>(gather, g, s, a);
+    else if (NH == 4)
+        launch_long_delta<4, 4>(gather, g, s, a);
+    else
+        return LORA_ERR_UNSPECIFIED;
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
+}
+
 // The delta of one family once the common arguments are checked: the
 // one-kernel path (or its split-K form, when a workspace is given and AUTO
 // wants it) or the two-kernel path through the workspace.
@@ -2424,16 +3160,21 @@ lora_status_t run_delta(const Common& c, const void* x, int64_t ldx, const void*
         }
         return run_fused(c, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
     }
-    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
+    const ShrinkChoice ch = choose_shrink(c, path);
+    if (path == LORA_PATH_AUTO && long_delta_wanted(c, ch)) {
+        st = run_long_delta(c, ch, x, ldx, A_stack, B_stack, bias_stack, y, ldy, s);
+        if (st != LORA_ERR_UNSPECIFIED)
+            return st;
+    }
     if (!workspace)
         return LORA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < delta_workspace(plan))
+    if (workspace_bytes < shrink_need(c, ch, true))
         return LORA_ERR_CAPACITY;
     float* slabs = reinterpret_cast<float*>(workspace);
-    st = run_shrink(c, plan, x, ldx, A_stack, slabs, path, s);
+    st = run_shrink_any(c, ch, x, ldx, A_stack, slabs, path, s);
     if (st != LORA_OK)
         return st;
-    int S = plan.S;
+    int S = ch.S();
     const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
     // Fold the slabs into slab 0 first on long batches: every feature tile
     // of the expand would otherwise read all S slabs of its token tile, while
@@ -2512,8 +3253,8 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
     if (!x || !A_stack || !u || !row_ok(ldx, c.fs.in_f, c.fs.elem) || !rows_fit(c, ldx) || !aligned16(x) ||
         !aligned16(A_stack) || !aligned16(u))
         return LORA_ERR_INVALID_ARGUMENT;
-    const ShrinkPlan plan = plan_shrink(c.fs, c.r.end, c.r.G);
-    const size_t need = shrink_workspace(plan);
+    const ShrinkChoice ch = choose_shrink(c, path);
+    const size_t need = shrink_need(c, ch, false);
     if (need > 0) {
         if (!workspace || !aligned16(workspace))
             return LORA_ERR_INVALID_ARGUMENT;
@@ -2521,13 +3262,14 @@ lora_status_t lora_sgmv_shrink(const lora_dims_t* dims, int32_t family, const vo
             return LORA_ERR_CAPACITY;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float* out = plan.S > 1 ? reinterpret_cast<float*>(workspace) : u;
-    st = run_shrink(c, plan, x, ldx, A_stack, out, path, s);
-    if (st != LORA_OK || plan.S == 1)
+    const int S = ch.S();
+    float* out = S > 1 ? reinterpret_cast<float*>(workspace) : u;
+    st = run_shrink_any(c, ch, x, ldx, A_stack, out, path, s);
+    if (st != LORA_OK || S == 1)
         return st;
     const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
     hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       s, out, n4, plan.S, u, n4);
+                       s, out, n4, S, u, n4);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
@@ -2579,8 +3321,11 @@ lora_status_t lora_sgmv_delta_noalloc(const lora_dims_t* dims, int32_t family, c
         return st;
     // the two-kernel path's partial sums must fit the scratch array
     const bool fused = path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && fused_auto(c));
-    if (!fused && delta_workspace(plan_shrink(c.fs, c.r.end, c.r.G)) > kScratchBytes)
-        return LORA_ERR_CAPACITY;
+    if (!fused) {
+        const ShrinkChoice ch = choose_shrink(c, path);
+        if (!(path == LORA_PATH_AUTO && long_delta_wanted(c, ch)) && shrink_need(c, ch, true) > kScratchBytes)
+            return LORA_ERR_CAPACITY;
+    }
     void* ws = scratch_address();
     if (!ws)
         return LORA_ERR_DEVICE;

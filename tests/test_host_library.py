@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert srg.lora_abi_version() == 8
+    assert srg.lora_abi_version() == 9
     assert srg.lora_status_string(0) == "LORA_OK"
     assert srg.lora_status_string(3) == "LORA_ERR_SLOT_OUT_OF_RANGE"
     assert srg.lora_status_string(99) == "LORA_ERR_UNKNOWN"

@@ -51,8 +51,10 @@ def _check_pair(name, keep, path, options, with_oracle):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("first,second,path,options", [
-    # two-kernel path: the shrink's K-split partial sums live in the scratch
+    # prefill: AUTO's one-kernel delta for long groups (no scratch)
     (("prefill", None), ("prefill", 5), srg.PATH_AUTO, None),
+    # two-kernel path: the shrink's K-split partial sums live in the scratch
+    (("stack", None), ("stack", 8), srg.PATH_AUTO, None),
     (("mixed", None), ("mixed", 60), srg.PATH_MFMA, None),
     # one-kernel path in its split-K form (partial sums in the scratch)
     (("decode", None), ("decode", 100), srg.PATH_AUTO, srg.LoraOptions(splitk_short=1)),
