@@ -89,6 +89,12 @@ def parse():
                    help="write profiles/traffic.json from the counter_collection.csv files of two "
                         "--counters runs (FETCH_SIZE, then WRITE_SIZE); needs no GPU")
     p.add_argument("--traffic-kind", default="delta_qkv")
+    p.add_argument("--counter-summary", nargs="+", metavar="CSV", default=None,
+                   help="print per-kernel means of the counters in rocprofv3 --pmc counter_collection.csv "
+                        "files and the derived MFMA / VALU / L2 figures; needs no GPU")
+    p.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"), default=None,
+                   help="print the kernel table of a rocprofv3 --kernel-trace --stats -f csv run and the "
+                        "library's kernels split by launch grid; needs no GPU")
     return p.parse_args()
 
 
@@ -148,6 +154,114 @@ def summarize_traffic(args):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out["kernels"]), flush=True)
+
+
+MI355X_SIMDS = 256 * 4  # compute units x SIMDs per CU
+MI355X_XCDS = 8
+L2_LINE = 128           # bytes per L1 -> L2 read request (one cache line)
+
+
+def counter_summary(paths):
+    """Per-kernel means of every counter in rocprofv3 --pmc CSV files (the
+    library's kernels only) and derived figures:
+      mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x SIMDs):
+        the share of the kernel's time the matrix cores were busy, chip-wide;
+      mfma_bf16_flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the counter
+        counts adds and multiplies in units of 512) per dispatch;
+      l1_to_l2_read_bytes = TCP_TCC_READ_REQ_sum x 128 (one line per request);
+      l2_hit_rate = TCC_HIT / (TCC_HIT + TCC_MISS)."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if "lora::" not in name:
+                    continue
+                short = name.split("(anonymous namespace)::")[1].split("(lora")[0] if "namespace)::" in name else name
+                key = f"{short} grid={r.get('Grid_Size', '?')}"
+                vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                try:
+                    dur[key].append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3)
+                except (KeyError, ValueError):
+                    pass
+    out = {}
+    for key in sorted(vals):
+        c = {k: float(np.mean(v)) for k, v in vals[key].items()}
+        d = {"counters": c, "dispatches": max(len(v) for v in vals[key].values())}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE accumulates over the 8 XCDs (it reads 8x the
+            # dispatch's duration x clock); the MFMA busy cycles over all SIMDs
+            d["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / MI355X_XCDS * MI355X_SIMDS)
+        if "TCP_TCC_READ_REQ_sum" in c:
+            d["l1_to_l2_read_bytes"] = c["TCP_TCC_READ_REQ_sum"] * L2_LINE
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            d["mfma_bf16_flops"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        if "TCC_HIT_sum" in c and c.get("TCC_HIT_sum", 0) + c.get("TCC_MISS_sum", 0) > 0:
+            d["l2_hit_rate"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+        out[key] = d
+        print(key, json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()
+                               if k != "counters"}), json.dumps({k: round(v, 1) for k, v in c.items()}),
+              flush=True)
+    return out
+
+
+def _short_kernel(name, width=62):
+    name = name.replace("(anonymous namespace)::", "")
+    name = name.split("(lora::")[0]
+    if name.endswith("(long)"):
+        name = name[:-len("(long)")]
+    return name[:width]
+
+
+def trace_summary(stats_csv, trace_csv):
+    """The kernel statistics of a rocprofv3 --kernel-trace --stats -f csv run
+    (every dispatch of the run), then the library's kernels split by launch
+    grid (workgroups x workgroup size), which separates the families and
+    call kinds that share one kernel instantiation."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    print(f"{'kernel':62s} {'calls':>8s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>8s}")
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            print(f"{_short_kernel(r['Name']):62s} {int(r['Calls']):8d} {float(r['AverageNs']) / 1e3:10.2f} "
+                  f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+    print()
+    print("Library kernels split by launch grid (workgroups x workgroup size):")
+    print()
+    grids = defaultdict(list)
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            if "lora::" not in r["Kernel_Name"]:
+                continue
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r.get("Workgroup_Size_Z", 1))
+            n = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // wg
+            grids[(_short_kernel(r["Kernel_Name"]), n, wg)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"{'kernel':62s} {'wgs':>6s} {'wg':>5s} {'calls':>7s} {'avg_us':>10s} {'median_us':>10s}")
+    for (n, nwg, wg), d in sorted(grids.items(), key=lambda kv: -len(kv[1])):
+        print(f"{n:62s} {nwg:6d} {wg:5d} {len(d):7d} {statistics.mean(d):10.2f} {statistics.median(d):10.2f}")
+
+
+def cpu_identity() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, vendor, family,
+    model and stepping (some virtual machines shorten the model name)."""
+    fields = {}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if not line.strip():
+                    break
+                k, _, v = line.partition(":")
+                fields.setdefault(k.strip(), v.strip())
+    except OSError:
+        return "unknown"
+    return (f"{fields.get('model name', '?')} ({fields.get('vendor_id', '?')}, family "
+            f"{fields.get('cpu family', '?')}, model {fields.get('model', '?')}, stepping "
+            f"{fields.get('stepping', '?')})")
 
 
 def kernel_sha() -> str:
@@ -462,6 +576,12 @@ def main():
     if args.traffic_from:
         summarize_traffic(args)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this benchmark measures one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only)", file=sys.stderr, flush=True)
@@ -639,6 +759,11 @@ def main():
         # bound the rows per call for the long workloads (about 0.1-1 s each)
         f0 = FAMS[0][0]
         budget = max(1, int(2e8 // (fam_shape[f0][0] * fam_shape[f0][1] * R + fam_shape[f0][3] * R)))
+        # the oracle is single-threaded C; run it on one host CPU (this
+        # thread's affinity only, restored afterwards)
+        host_cpus = os.sched_getaffinity(0)
+        pin_cpu = min(host_cpus)
+        os.sched_setaffinity(0, {pin_cpu})
         while t_cpu < args.cpu_seconds and n_calls < 100000:
             l = n_calls % n_distinct
             if l >= len(prepared):
@@ -681,17 +806,14 @@ def main():
             t_cpu += time.perf_counter() - t0
             tokens_done += sum(len(rows[i]) for i in reqs)
             n_calls += 1
-        cpu_model = None
-        try:
-            with open("/proc/cpuinfo") as fh:
-                cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
-        except OSError:
-            pass
+        os.sched_setaffinity(0, host_cpus)
         cpu = {"value": tokens_done / t_cpu, "unit": "LoRA tokens x layers / s", "cores": 1,
-               "kind": "oracle", "cpu_model": cpu_model, "host_cpus_available": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "cpu_model": cpu_identity(), "pinned_cpu": pin_cpu,
+               "host_cpus_available": len(host_cpus),
                "sample": f"{tokens_done} LoRA-routed token rows through the {proj_desc} delta of one layer "
                          f"({n_calls} oracle passes over {len(prepared)} distinct layers of the same "
-                         f"workload, at most {budget} rows per pass), fp64, single thread, {t_cpu:.1f} s"}
+                         f"workload, at most {budget} rows per pass), fp64, one thread pinned to host "
+                         f"CPU {pin_cpu}, {t_cpu:.1f} s"}
         log(f"phase 3: oracle {cpu['value']:.1f} tokens x layers/s")
 
     out = {
