@@ -690,14 +690,19 @@ __global__ __launch_bounds__(kThreads) void reduce_slabs(const float* P, int64_t
 // One 512-thread workgroup owns a piece of at most 64 consecutive tokens of
 // one group, one group of at most 16 NB columns of u, and one K range
 // [kb, ke) (all of K unless the launch splits K).  Its 8 waves split the K
-// range; wave w streams the piece's 64 rows of x over its K share, and the
-// matching A rows, straight into registers, P 32-element steps ahead of the
-// matrix instructions, with no LDS and no barrier in the loop.  Per step the
-// wave issues four x loads (16 rows x 64 bytes each, the M operands of the
-// four 16-row blocks) and NB A loads (16 columns x 32 K values each, one
-// contiguous 1 KB run of the tiled layout: the N operands), then 4 NB
-// v_mfma_f32_16x16x32_bf16.  K positions past the range and rows past the
-// piece read zero through the buffer bounds.  The 8 partial tiles are then
+// range; wave w streams the piece's 64 rows of x over its K share in chunks
+// of 64 K values, D chunks ahead of the matrix instructions, with no barrier
+// in the loop.  A chunk is eight loads of whole 128-byte lines (8 rows x 128
+// B each; the matrix layout would split every line over two loads, which
+// streams about 20 % slower on this part) into registers, written into the
+// wave's own 8 KB LDS region with the 16-byte pieces rotated by row (so that
+// the line writes and the fragment reads spread over the banks), from which
+// the wave reads the M operands of its four 16-row blocks.  The A fragments
+// (16 columns x 32 K values each, one contiguous 1 KB run of the tiled
+// layout: the N operands) come straight into registers.  Per 32-element step
+// the wave runs 4 NB v_mfma_f32_16x16x32_bf16.  K positions past the range
+// and rows past the piece read zero through the buffer bounds.  The 8
+// partial tiles are then
 // added in LDS in a fixed tree order ((w0 + w4) + (w2 + w6)) + ((w1 + w5) +
 // (w3 + w7)), so the result is deterministic, and written to u, or to slab s
 // of the workspace when K is split.
@@ -709,6 +714,10 @@ __global__ __launch_bounds__(kThreads) void reduce_slabs(const float* P, int64_t
 // in contiguous runs, so a group's A rows are fetched into few L2s.
 constexpr int kLsWaves = 8;
 constexpr int kLsThreads = 64 * kLsWaves;
+constexpr int kLdWaveBytes = 64 * 128;  // a wave's LDS region: 64 rows x 128 B
+
+// byte offset in a wave's region of 16-byte piece p (0..7) of row r
+__device__ __forceinline__ int ld_slot(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
 constexpr int kLsRows = 64;               // tokens of a piece: four 16-row MFMA blocks
 constexpr int kLsKUnit = 32 * kLsWaves;   // K split granularity: one step of every wave
 
@@ -766,13 +775,16 @@ struct LongShrinkLds {
     static constexpr int kLd = 16 * NB + 4;          // padded row of a partial tile (floats)
     static constexpr int kTile = kLsRows * kLd;      // one wave's partial tile
     static constexpr int kFloats = 4 * kTile;        // four tiles in flight in the tree
+    // the waves' regions during the K loop, the tree after it
+    static constexpr int kBytes = kLsWaves * kLdWaveBytes > kFloats * 4 ? kLsWaves * kLdWaveBytes : kFloats * 4;
 };
 
-template <int NB, int P, bool GATHER>
+template <int NB, int D, bool GATHER>
 __global__ __launch_bounds__(kLsThreads) void shrink_long_kernel(LongShrinkArgs a)
 {
     typedef LongShrinkLds<NB> Lay;
-    __shared__ __attribute__((aligned(16))) float red[Lay::kFloats];
+    __shared__ __attribute__((aligned(16))) char smem[Lay::kBytes];
+    float* red = reinterpret_cast<float*>(smem);
     asm volatile("" ::"s"(a.x), "s"(a.ldx), "s"(a.A), "s"(a.a_slot), "s"(a.out), "s"(a.slab), "s"(a.in_f),
                  "s"(a.C), "s"(a.kc), "s"(a.zs), "s"(a.S), "s"(a.cb), "s"(a.per_xcd), "s"(a.pieces), "s"(a.r.G),
                  "s"(a.r.kr));
@@ -789,62 +801,77 @@ __global__ __launch_bounds__(kLsThreads) void shrink_long_kernel(LongShrinkArgs 
     const int c0 = z * a.cb, cw = min(a.cb, a.C - c0);
     const int kb = s * a.kc, ke = min(kb + a.kc, a.in_f);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int lr = lane >> 3, lp = lane & 7;  // whole-line layout: row lr + 8 i, 16-byte piece lp
+    char* region = smem + w * kLdWaveBytes;
     const int kw = a.kc / kLsWaves;
     const int k0 = kb + w * kw, k1 = min(k0 + kw, ke);
-    const int nsteps = k1 > k0 ? (k1 - k0 + 31) >> 5 : 0;
+    const int nch = k1 > k0 ? (k1 - k0 + 63) >> 6 : 0;
 
     const RowMap<GATHER> xm{a.r.rows, ti.t0, ti.n, a.r.nrows};
     const Buf xb = xm.buf(a.x, a.ldx);
-    uint32_t xrow[4];
+    uint32_t xro[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        xrow[m] = (uint32_t)(xm(16 * m + l16) * a.ldx) * 2;
+    for (int i8 = 0; i8 < 8; ++i8)
+        xro[i8] = (uint32_t)(xm(lr + 8 * i8) * a.ldx) * 2;
     const Buf ab(a.A + (size_t)ti.slot * a.a_slot + (size_t)(c0 >> 4) * 16 * a.in_f,
                  (uint32_t)(((cw + 15) >> 4) * 16 * a.in_f * 2));
     const uint32_t ablk = (uint32_t)(16 * a.in_f) * 2;
 
-    uint4 xr[P][4], ar[P][NB];
     f32x4_t acc[4][NB];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto load = [&](int st, uint4(&xv)[4], uint4(&av)[NB]) {
-        const int kk = k0 + 32 * st + 8 * q;
-        const bool ok = kk < k1;
+    uint4 xs[D][8], as[D][2][NB];
+    auto load = [&](int ch, uint4(&xv)[8], uint4(&av)[2][NB]) {
+        const int kx = k0 + 64 * ch + 8 * lp;
+        const bool okx = kx < k1;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            xv[m] = xb.ld16(ok ? xrow[m] + (uint32_t)kk * 2 : kOOB);
-        const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 16);
+        for (int i8 = 0; i8 < 8; ++i8)
+            xv[i8] = xb.ld16(okx ? xro[i8] + (uint32_t)kx * 2 : kOOB);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            av[nb] = ab.ld16(ok ? nb * ablk + ao : kOOB);
+        for (int h = 0; h < 2; ++h) {
+            const int kk = k0 + 64 * ch + 32 * h + 8 * q;
+            const uint32_t ao = (uint32_t)(((kk >> 3) * 16 + l16) * 16);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                av[h][nb] = ab.ld16(kk < k1 ? nb * ablk + ao : kOOB);
+        }
     };
-    // the prologue issues the steps in slot order too, so that at the loop
+    // the prologue issues the chunks in slot order too, so that at the loop
     // head slot j's loads are as old along both incoming edges
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-        load(j, xr[j], ar[j]);
+    for (int j = 0; j < D; ++j) {
+        load(j, xs[j], as[j]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int base = 0; base < nsteps; base += P) {
+    for (int base = 0; base < nch; base += D) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
+        for (int j = 0; j < D; ++j) {
+            // whole lines into the wave's region, then the M operands out of it
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int i8 = 0; i8 < 8; ++i8)
+                *reinterpret_cast<uint4*>(region + ld_slot(lr + 8 * i8, lp)) = xs[j][i8];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[j][m]),
-                                                                        __builtin_bit_cast(bf16x8_t, ar[j][nb]),
-                                                                        acc[m][nb], 0, 0, 0);
-            load(base + P + j, xr[j], ar[j]);
-            // keep each step's reload right after its matrix instructions:
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 xf = *reinterpret_cast<const uint4*>(region + ld_slot(16 * m + l16, 4 * h + q));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xf), __builtin_bit_cast(bf16x8_t, as[j][h][nb]), acc[m][nb],
+                            0, 0, 0);
+                }
+            load(base + D + j, xs[j], as[j]);
+            // keep each chunk's reload right after its matrix instructions:
             // left alone, the scheduler sinks every reload to the end of the
             // body and the loop head then waits for all of them
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    __syncthreads();  // every wave is done with its region before the tree reuses it
 
     // D of block (m, nb): lane holds column 16 nb + l16 of rows 16 m + 4 q + r
     auto put = [&](int t) {
@@ -1556,8 +1583,6 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a)
 // bias, writes the rounded result back in place, and stores it as whole
 // lines.  All accesses of x and y go through buffer bounds: rows past the
 // piece read zero and drop their stores.
-constexpr int kLdWaveBytes = 64 * 128;  // a wave's LDS region: 64 rows x 128 B
-
 struct LongDeltaArgs {
     const uint16_t* x;
     int64_t ldx;
@@ -1583,9 +1608,6 @@ struct LongDeltaLds {
     static constexpr int kU = (kRegions > kRed ? kRegions : kRed);  // offset of u [64][16 NB] fp32
     static constexpr int kBytes = kU + kLsRows * 16 * NB * 4;
 };
-
-// byte offset in a wave's region of 16-byte piece p (0..7) of row r
-__device__ __forceinline__ int ld_slot(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
 
 template <int NB, int NH, int D, int D2, bool GATHER>
 __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
@@ -2579,10 +2601,10 @@ template <bool G>
 hipError_t launch_shrink_long(const LongShrinkArgs& a, int nb, dim3 grid, hipStream_t st)
 {
     switch (nb) {
-    case 1: hipLaunchKernelGGL((shrink_long_kernel<1, 8, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((shrink_long_kernel<2, 6, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((shrink_long_kernel<3, 4, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((shrink_long_kernel<4, 4, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((shrink_long_kernel<1, 3, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_long_kernel<2, 3, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((shrink_long_kernel<3, 2, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_long_kernel<4, 2, G>), grid, dim3(kLsThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }
