@@ -2559,12 +2559,12 @@ ShrinkChoice choose_shrink(const Common& c, int32_t path)
     ShrinkChoice ch;
     const int64_t tiles = long_tiles(c);
     ch.lp = plan_long(c.fs, tiles);
-    // the long-segment kernel only where its plan splits no K and u has one
-    // column group (batches that fill the chip with 64-token pieces): with a
-    // K split, the 256-thread kernel measured faster (mixed batch 24.2
-    // against 30.0 us), and so it did with two column groups (32-layer stack
-    // QKV, rank 32: delta_qkv 49.0 against 51.5 us, pieces of ~28 tokens)
-    ch.lng = shrink_mfma_ok(c) && path != LORA_PATH_VALU && ch.lp.S == 1 && ch.lp.nz == 1;
+    // the long-segment kernel only where its plan splits no K (batches that
+    // fill the chip with 64-token pieces): with a K split, the 256-thread
+    // kernel measured faster (mixed batch 24.2 against 30.0 us).  The 32-layer
+    // stack's rank-32 QKV (two column groups, pieces of ~28 tokens) takes it:
+    // delta_qkv 47.4 against 49.1 us with the 256-thread kernel
+    ch.lng = shrink_mfma_ok(c) && path != LORA_PATH_VALU && ch.lp.S == 1;
     if (!ch.lng)
         ch.old = plan_shrink(c.fs, c.r.end, c.r.G);
     // the pieces of the long-segment kernels (the long delta may be forced
