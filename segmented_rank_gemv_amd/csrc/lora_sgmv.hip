@@ -1609,7 +1609,19 @@ struct LongDeltaLds {
     static constexpr int kBytes = kU + kLsRows * 16 * NB * 4;
 };
 
-template <int NB, int NH, int D, int D2, bool GATHER>
+// g holds one 16-byte fragment in lanes 0..31 and another in lanes 32..63;
+// lo gets the first in every lane, hi the second (v_permlane32_swap).
+__device__ __forceinline__ void permlane32_split(uint4 g, uint4& lo, uint4& hi)
+{
+    const auto sx = __builtin_amdgcn_permlane32_swap(g.x, g.x, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(g.y, g.y, false, false);
+    const auto sz = __builtin_amdgcn_permlane32_swap(g.z, g.z, false, false);
+    const auto sw = __builtin_amdgcn_permlane32_swap(g.w, g.w, false, false);
+    lo = make_uint4(sx[0], sy[0], sz[0], sw[0]);
+    hi = make_uint4(sx[1], sy[1], sz[1], sw[1]);
+}
+
+template <int NB, int NH, int D, int D2, bool HB, bool GATHER>
 __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
 {
     typedef LongDeltaLds<NB, NH> Lay;
@@ -1776,8 +1788,12 @@ __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);  // permuted M row of block 0 (see expand_mfma)
     const int fb = w * a.fw, fe = min(fb + a.fw, a.out_f);
     const int ntl = fe > fb ? (fe - fb) >> 6 : 0;
-    uint4 ys[D2][8], bs[D2][2][2][NH], bis[D2][2];
-    auto load_y = [&](int t, uint4(&yv)[8], uint4(&bv)[2][2][NH], uint4(&biv)[2]) {
+    // B fragments: lanes q < 2 fetch the rows of the first 4-row half (hh =
+    // 0), lanes q >= 2 those of the second; a permlane32 swap then gives
+    // every lane both (the two halves of a wave need the same fragments),
+    // which halves the B loads
+    uint4 ys[D2][8], bs[D2][2][NH], bis[D2][2];
+    auto load_y = [&](int t, uint4(&yv)[8], uint4(&bv)[2][NH], uint4(&biv)[2]) {
         const int f = fb + 64 * t;
         const bool ok = t < ntl;
 #pragma unroll
@@ -1786,12 +1802,11 @@ __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int kh = 0; kh < NH; ++kh)
-                    bv[h][hh][kh] =
-                        bb.ld16(ok ? (uint32_t)((f + 32 * h + mrow + 4 * hh) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
-            biv[h] = biasb.ld16(ok ? (uint32_t)(f + 32 * h + 8 * q) * 2 : kOOB);
+            for (int kh = 0; kh < NH; ++kh)
+                bv[h][kh] = bb.ld16(
+                    ok ? (uint32_t)((f + 32 * h + mrow + 4 * (q >> 1)) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+            if constexpr (HB)
+                biv[h] = biasb.ld16(ok ? (uint32_t)(f + 32 * h + 8 * q) * 2 : kOOB);
         }
     };
 #pragma unroll
@@ -1843,14 +1858,16 @@ __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
                         const uint4 yv = *cell;
                         f32x4_t acc0 = {bf2f(yv.x & 0xFFFFu), bf2f(yv.x >> 16), bf2f(yv.y & 0xFFFFu), bf2f(yv.y >> 16)};
                         f32x4_t acc1 = {bf2f(yv.z & 0xFFFFu), bf2f(yv.z >> 16), bf2f(yv.w & 0xFFFFu), bf2f(yv.w >> 16)};
-                        if (a.bias)
+                        if constexpr (HB)
                             add_bias8(bis[j][h], acc0, acc1);
 #pragma unroll
                         for (int kh = 0; kh < NH; ++kh) {
-                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bs[j][h][0][kh]),
-                                                                          uf[m][kh], acc0, 0, 0, 0);
-                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bs[j][h][1][kh]),
-                                                                          uf[m][kh], acc1, 0, 0, 0);
+                            uint4 b0, b1;
+                            permlane32_split(bs[j][h][kh], b0, b1);
+                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[m][kh],
+                                                                          acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[m][kh],
+                                                                          acc1, 0, 0, 0);
                         }
                         uint4 o;
                         o.x = f2bf_pair(acc0[0], acc0[1]);
@@ -3107,10 +3124,14 @@ void launch_long_delta(bool gather, dim3 grid, hipStream_t s, const LongDeltaArg
 {
     constexpr int D = NB <= 2 ? 3 : 2;
     constexpr int D2 = NH <= 2 ? 2 : 1;
-    if (gather)
-        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, true>), grid, dim3(kLsThreads), 0, s, a);
+    if (gather && a.bias)
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, true, true>), grid, dim3(kLsThreads), 0, s, a);
+    else if (gather)
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, false, true>), grid, dim3(kLsThreads), 0, s, a);
+    else if (a.bias)
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, true, false>), grid, dim3(kLsThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, false>), grid, dim3(kLsThreads), 0, s, a);
+        hipLaunchKernelGGL((delta_long_kernel<NB, NH, D, D2, false, false>), grid, dim3(kLsThreads), 0, s, a);
 }
 
 lora_status_t run_long_delta(const Common& c, const ShrinkChoice& ch, const void* x, int64_t ldx,
