@@ -51,7 +51,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-REPLICAS = {"tiny": 1, "decode": 64, "prefill": 2, "mixed": 8, "stack": 32, "mlp": 32}
+REPLICAS = {"tiny": 1, "decode": 64, "prefill": 4, "mixed": 8, "stack": 32, "mlp": 32}
 KERNEL_SRC = os.path.join(ROOT, "segmented_rank_gemv_amd", "csrc", "lora_sgmv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

@@ -33,6 +33,7 @@
 // results.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <mutex>
 #include <string.h>
@@ -87,8 +88,10 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Cache policy bits of an access (kKeep: default; kStream: non-temporal).
-// Measured on MI355X, non-temporal x / y accesses slowed both kernels, so
-// every access uses kKeep.
+// The one-kernel long delta reads x non-temporally (x is read once there,
+// and kept out of the caches it no longer pushes the previous call's y
+// lines out); everything else uses kKeep, which measured faster for the
+// split kernels' x and y.
 enum CachePolicy { kKeep = 0, kStream = 2 };
 
 template <int POL = kKeep>
@@ -96,6 +99,11 @@ struct BufT {
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ BufT(const void* base, uint32_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000))
+    {
+    }
+    // the same buffer with another cache policy
+    template <int P2>
+    __device__ __forceinline__ explicit BufT(const BufT<P2>& o) : r(o.r)
     {
     }
     __device__ __forceinline__ uint4 ld16(uint32_t off) const
@@ -779,7 +787,7 @@ struct LongShrinkLds {
     static constexpr int kBytes = kLsWaves * kLdWaveBytes > kFloats * 4 ? kLsWaves * kLdWaveBytes : kFloats * 4;
 };
 
-template <int NB, int D, bool GATHER>
+template <int NB, int D, bool NTX, bool GATHER>
 __global__ __launch_bounds__(kLsThreads) void shrink_long_kernel(LongShrinkArgs a)
 {
     typedef LongShrinkLds<NB> Lay;
@@ -808,7 +816,9 @@ __global__ __launch_bounds__(kLsThreads) void shrink_long_kernel(LongShrinkArgs 
     const int nch = k1 > k0 ? (k1 - k0 + 63) >> 6 : 0;
 
     const RowMap<GATHER> xm{a.r.rows, ti.t0, ti.n, a.r.nrows};
-    const Buf xb = xm.buf(a.x, a.ldx);
+    // with one column group x is read once: non-temporal (NTX)
+    typedef typename std::conditional<NTX, StreamBuf, Buf>::type XBuf;
+    const XBuf xb(xm.buf(a.x, a.ldx));
     uint32_t xro[8];
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8)
@@ -1668,7 +1678,7 @@ __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
     const RowMap<GATHER> rm{a.r.rows, ti.t0, ti.n, a.r.nrows};
 
     // ---------------- phase 1: u = A . x over the wave's K range
-    const Buf xb = rm.buf(a.x, a.ldx);
+    const StreamBuf xb(rm.buf(a.x, a.ldx));  // x is read once: non-temporal
     uint32_t xro[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -2614,14 +2624,14 @@ size_t shrink_need(const Common& c, const ShrinkChoice& ch, bool delta)
     return (delta || S > 1) ? (size_t)S * ch.slab_bytes(c) : 0;
 }
 
-template <bool G>
+template <bool NTX, bool G>
 hipError_t launch_shrink_long(const LongShrinkArgs& a, int nb, dim3 grid, hipStream_t st)
 {
     switch (nb) {
-    case 1: hipLaunchKernelGGL((shrink_long_kernel<1, 3, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((shrink_long_kernel<2, 3, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((shrink_long_kernel<3, 2, G>), grid, dim3(kLsThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((shrink_long_kernel<4, 2, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((shrink_long_kernel<1, 3, NTX, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((shrink_long_kernel<2, 3, NTX, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((shrink_long_kernel<3, 2, NTX, G>), grid, dim3(kLsThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((shrink_long_kernel<4, 2, NTX, G>), grid, dim3(kLsThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }
@@ -2653,8 +2663,15 @@ lora_status_t run_shrink_long(const Common& c, const ShrinkChoice& ch, const voi
     if (grid == 0)
         return LORA_OK;
     const int nb = ch.lp.cb / 16;
-    const hipError_t e = c.r.rows ? launch_shrink_long<true>(a, nb, dim3((unsigned)grid), s)
-                                  : launch_shrink_long<false>(a, nb, dim3((unsigned)grid), s);
+    // one column group reads x once: non-temporal x loads (prefill, 4
+    // layers: shrink_qkv 28.6 -> 25.3 us, shrink_o 26.6 -> 21.7 us); with
+    // two, the second group's reads hit the caches the first one filled
+    const dim3 g((unsigned)grid);
+    const bool ntx = ch.lp.nz == 1;
+    const hipError_t e = c.r.rows ? (ntx ? launch_shrink_long<true, true>(a, nb, g, s)
+                                         : launch_shrink_long<false, true>(a, nb, g, s))
+                                  : (ntx ? launch_shrink_long<true, false>(a, nb, g, s)
+                                         : launch_shrink_long<false, false>(a, nb, g, s));
     return e == hipSuccess ? LORA_OK : LORA_ERR_DEVICE;
 }
 
