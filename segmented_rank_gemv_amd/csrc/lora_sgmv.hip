@@ -88,10 +88,11 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Cache policy bits of an access (kKeep: default; kStream: non-temporal).
-// The one-kernel long delta reads x non-temporally (x is read once there,
-// and kept out of the caches it no longer pushes the previous call's y
-// lines out); everything else uses kKeep, which measured faster for the
-// split kernels' x and y.
+// The long-group kernels touch x (and the one-kernel delta y) once, and
+// access them non-temporally: kept out of the caches they no longer push
+// out the lines the next call would otherwise have to write back first
+// (prefill step, 4 layers: 0.653 -> 0.611 ms).  The other kernels re-read
+// x or y across workgroups and use kKeep.
 enum CachePolicy { kKeep = 0, kStream = 2 };
 
 template <int POL = kKeep>
@@ -1788,7 +1789,7 @@ __global__ __launch_bounds__(kLsThreads) void delta_long_kernel(LongDeltaArgs a)
     __syncthreads();
 
     // ---------------- phase 2: y += B . u (+ bias) over the wave's features
-    const Buf yb = rm.buf(a.y, a.ldy);
+    const StreamBuf yb(rm.buf(a.y, a.ldy));  // y is read and written once: non-temporal
     uint32_t yro[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
