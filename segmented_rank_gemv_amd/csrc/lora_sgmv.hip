@@ -91,8 +91,10 @@ constexpr uint32_t kOOB = 0x80000000u;
 // The long-group kernels touch x (and the one-kernel delta y) once, and
 // access them non-temporally: kept out of the caches they no longer push
 // out the lines the next call would otherwise have to write back first
-// (prefill step, 4 layers: 0.653 -> 0.611 ms).  The other kernels re-read
-// x or y across workgroups and use kKeep.
+// (prefill step, 4 layers: 0.653 -> 0.611 ms).  So does the rank-16 MFMA
+// expand with y (prefill split API step 0.646 -> 0.606 ms).  The same
+// policy measured slower on the decode kernel's x and on the rank-32/64
+// expand's y (32-layer stack +5 %), which keep kKeep.
 enum CachePolicy { kKeep = 0, kStream = 2 };
 
 template <int POL = kKeep>
@@ -1109,6 +1111,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
                                             const Buf& yb, const RowMap<GATHER>& ym, int ucol0, float* us,
                                             float4* part, uint16_t* ylds, uint16_t* blds, uint16_t* bls)
 {
+    const StreamBuf ybn(yb);  // y is read and written once: non-temporal
     static_assert(NH == 1 || NH == 2 || NH == 4, "B chunk swizzle needs a power-of-two chunk count");
     constexpr int R = 16 * NH;
     constexpr int NCH = R / 8;                      // 16-byte chunks per B row
@@ -1141,7 +1144,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
 #pragma unroll
     for (int i = 0; i < kMaxPairs; ++i) {
         const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
-        yraw[i] = yb.ld16(i < np ? (uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2 : kOOB);
+        yraw[i] = ybn.ld16(i < np ? (uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2 : kOOB);
     }
     // coalesced B tile: ft rows x NCH chunks (past the tile: kOOB)
     uint4 braw[BR];
@@ -1224,7 +1227,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
     for (int i = 0; i < kMaxPairs; ++i) {
         if (i < np) {
             const int p = tid + kThreads * i, row = p / pieces, pc = p - row * pieces;
-            yb.st16((uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2,
+            ybn.st16((uint32_t)(yrow_of(i, row) * a.ldy + f0 + 8 * pc) * 2,
                     *reinterpret_cast<const uint4*>(ylds + row * kYLd + 8 * pc));
         }
     }
