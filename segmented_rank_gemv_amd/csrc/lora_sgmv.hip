@@ -2007,12 +2007,12 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
     const bool tok = l16 < te.n;
     const RowMap<GATHER> rm{a.r.rows, te.t0, te.n, a.r.nrows};
     const uint32_t trow = rm(l16);
-    const Buf yb = rm.buf(a.y, a.ldy);
+    const StreamBuf yb(rm.buf(a.y, a.ldy));
     const Buf biasb(a.bias + (size_t)te.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
     const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint32_t yoff[NPAIR];
-    uint4 yraw[NPAIR], braw_bias[NPAIR], bfr[NPAIR][2][NH];
+    uint4 yraw[NPAIR], braw_bias[NPAIR], bfr[NPAIR][NH];
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {
         const int fp = 32 * (w + kFusedWaves * p);  // first feature of pair p in the tile
@@ -2023,10 +2023,8 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
         // B rows as the M operand, permuted: row i of block h is feature
         // fp + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kh = 0; kh < NH; ++kh)
-                bfr[p][h][kh] = bb.ld16(pv ? (uint32_t)((fp + mrow + 4 * h) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
+        for (int kh = 0; kh < NH; ++kh)
+            bfr[p][kh] = bb.ld16(pv ? (uint32_t)((fp + mrow + 4 * (q >> 1)) * R + 16 * kh + 8 * (q & 1)) * 2 : kOOB);
     }
     // u of the tile from the slabs: entry e is 4 floats of slab e / Q, token
     // row (e % Q) / (R / 4), columns 4 ((e % Q) % (R / 4)) .. + 3 of the
@@ -2079,10 +2077,10 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
             add_bias8(braw_bias[p], acc0, acc1);
 #pragma unroll
         for (int kh = 0; kh < NH; ++kh) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[p][0][kh]), uf[kh],
-                                                          acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[p][1][kh]), uf[kh],
-                                                          acc1, 0, 0, 0);
+            uint4 b0, b1;
+            permlane32_split(bfr[p][kh], b0, b1);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), uf[kh], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), uf[kh], acc1, 0, 0, 0);
         }
         uint4 o;
         o.x = f2bf_pair(acc0[0], acc0[1]);
