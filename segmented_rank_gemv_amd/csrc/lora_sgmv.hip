@@ -92,9 +92,10 @@ constexpr uint32_t kOOB = 0x80000000u;
 // access them non-temporally: kept out of the caches they no longer push
 // out the lines the next call would otherwise have to write back first
 // (prefill step, 4 layers: 0.653 -> 0.611 ms).  So does the rank-16 MFMA
-// expand with y (prefill split API step 0.646 -> 0.606 ms).  The same
-// policy measured slower on the decode kernel's x and on the rank-32/64
-// expand's y (32-layer stack +5 %), which keep kKeep.
+// expand with y (prefill split API step 0.646 -> 0.606 ms) and the expand
+// half of the split-K delta for short groups (MLP decode step 0.835 ->
+// 0.791 ms).  The same policy measured slower on the decode kernel's x and
+// on the rank-32/64 expand's y (32-layer stack +5 %), which keep kKeep.
 enum CachePolicy { kKeep = 0, kStream = 2 };
 
 template <int POL = kKeep>
@@ -2007,11 +2008,15 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
     const bool tok = l16 < te.n;
     const RowMap<GATHER> rm{a.r.rows, te.t0, te.n, a.r.nrows};
     const uint32_t trow = rm(l16);
-    const StreamBuf yb(rm.buf(a.y, a.ldy));
+    const StreamBuf yb(rm.buf(a.y, a.ldy));  // y is read and written once: non-temporal
     const Buf biasb(a.bias + (size_t)te.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
     const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint32_t yoff[NPAIR];
+    // B fragments: lanes q < 2 fetch the rows of the low 16 features of a
+    // pair, lanes q >= 2 those of the high 16; a permlane32 swap at use hands
+    // each half of the wave the rows it multiplies, so every fragment is
+    // fetched once per wave.
     uint4 yraw[NPAIR], braw_bias[NPAIR], bfr[NPAIR][NH];
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {
