@@ -42,6 +42,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -265,8 +266,15 @@ def cpu_identity() -> str:
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments, trailing blanks and empty
+    lines removed, so that an edit of a comment keeps counter figures taken
+    with the same code valid."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    tok = re.compile(r'("(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\')|//[^\n]*|/\*.*?\*/', re.S)
+    code = tok.sub(lambda m: m.group(1) or "", src)
+    lines = [ln.rstrip() for ln in code.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()[:16]
 
 
 def run_workload(args, torch, synth, srg, dev, log):

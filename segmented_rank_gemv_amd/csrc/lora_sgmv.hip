@@ -2013,10 +2013,10 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
     const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint32_t yoff[NPAIR];
-    // B fragments: lanes q < 2 fetch the rows of the low 16 features of a
-    // pair, lanes q >= 2 those of the high 16; a permlane32 swap at use hands
-    // each half of the wave the rows it multiplies, so every fragment is
-    // fetched once per wave.
+    // B fragments: lanes q < 2 fetch the rows of a pair's block 0 (the
+    // first MFMA), lanes q >= 2 those of block 1; a permlane32 swap at use
+    // gives every lane its row of each block, so every fragment is fetched
+    // once per wave.
     uint4 yraw[NPAIR], braw_bias[NPAIR], bfr[NPAIR][NH];
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {

@@ -53,3 +53,26 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # per call: (1000 + 10) KiB fetched x 2 + (20 + 5) KiB written
     want = (1010.0 * 2 + 25.0) * 1024
     assert out["kernels"]["prefill:shrink_qkv"]["hbm_bytes_per_launch"] == pytest.approx(want)
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """The hash that ties profiles/traffic.json to a kernel source changes with
+    the code and with string literals, not with comments or blank lines."""
+    import bench
+    base = ('// header\n#include <x.h>\n/* block\n   comment */\nint f(int a) { return a + 1; }  // tail\n'
+            'const char* s = "not // a comment";\n')
+    variants = {
+        "base": base,
+        "comments": base.replace("// header", "// another header\n\n").replace("// tail", "/* t */"),
+        "code": base.replace("a + 1", "a + 2"),
+        "string": base.replace("not // a comment", "not // a remark"),
+    }
+    h = {}
+    for k, src in variants.items():
+        p = tmp_path / f"{k}.hip"
+        p.write_text(src)
+        monkeypatch.setattr(bench, "KERNEL_SRC", str(p))
+        h[k] = bench.kernel_sha()
+    assert h["comments"] == h["base"]
+    assert h["code"] != h["base"]
+    assert h["string"] != h["base"]
