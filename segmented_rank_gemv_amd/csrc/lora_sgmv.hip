@@ -1977,8 +1977,8 @@ struct FusedArgs {
     int nsplit;      // kPartExpand: slabs to add (at most kFusedWaves)
     RouteArgs r;
     TileEntry tt[kFusedHostTiles];  // tiles built on the host (HOSTT launches)
-    int2 fts[kFusedHostFt];         // (slice, first feature) of each feature tile (HOSTT);
-                                    // SHRINK: (slice, K split)
+    int2 fts[kFusedHostFt];         // (slice | 32-feature pairs << 8, first feature) of each
+                                    // feature tile (HOSTT); SHRINK: (slice, K split)
 };
 
 // STEPS = K steps a wave keeps in flight per batch (register budget).
@@ -2019,7 +2019,7 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
     const int ftile = blockIdx.x / kXcds;
     const TileEntry te = a.tt[min(tile, kFusedHostTiles - 1)];
     const int2 fe = a.fts[min(ftile, kFusedHostFt - 1)];
-    const int sl = fe.x, f0 = fe.y;
+    const int sl = fe.x & 0xFF, f0 = fe.y;
     const uint32_t live = te.n > 0 ? 1u : 0u;  // 0 for a padding tile
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, q = lane >> 4;
@@ -2139,7 +2139,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const int tile = blockIdx.y * kXcds + blockIdx.x % kXcds;
     const int ftile = blockIdx.x / kXcds;
     TileInfo ti;
-    int sl = 0, f0;
+    int sl = 0, f0, fw = a.F;  // slice, first feature and width of the feature tile
     if constexpr (HOSTT) {
         // the entries' addresses depend on blockIdx only, and nothing branches
         // before the data loads: the argument loads take one round trip.  A
@@ -2151,7 +2151,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
         ti.n = te.n;
         ti.slot = te.slot;
         ti.glen = te.glen;
-        sl = fe.x;
+        sl = fe.x & 0xFF;
+        fw = 32 * (fe.x >> 8);
         f0 = fe.y;
         // every argument the data addresses need, in scalar registers before
         // anything else: the compiler would otherwise split the argument
@@ -2174,7 +2175,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const int l16 = lane & 15, q = lane >> 4;
 
     // --- issue the loads: the wave's y run and B rows, then x / A batches
-    const int np = a.F >> 5;
+    const int np = fw >> 5;
     const bool pair = w < np;
     const bool tok = l16 < ti.n;
     const RowMap<GATHER> rm{a.r.rows, ti.t0, ti.n, a.r.nrows};
@@ -2183,11 +2184,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_delta_kernel(FusedArgs a)
     const uint32_t yoff = (pair && tok) ? (uint32_t)(trow * a.ldy + f0 + 32 * w + 8 * q) * 2 : kOOB;
     const uint4 yraw = SHRINK ? make_uint4(0u, 0u, 0u, 0u) : yb.ld16(yoff);
     // the wave's 8 bias values, read with y (zero without a bias)
-    const Buf biasb(a.bias + (size_t)ti.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
+    const Buf biasb(a.bias + (size_t)ti.slot * a.out_f + f0, a.bias ? live * (uint32_t)(fw * 2) : 0u);
     const uint4 braw_bias = SHRINK ? make_uint4(0u, 0u, 0u, 0u) : biasb.ld16(pair ? (uint32_t)(32 * w + 8 * q) * 2 : kOOB);
     // B rows as the M operand, permuted: row i of block h is feature
     // 32 w + 8 (i / 4) + 4 h + i % 4 (see expand_mfma)
-    const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
+    const Buf bb(a.B + ((size_t)ti.slot * a.out_f + f0) * R, live * (uint32_t)(fw * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint4 bfr[2][NH];
 #pragma unroll
@@ -2915,11 +2916,17 @@ int fused_widest_feat(const Common& c)
 // read.  So the tile is halved (down to 128 features) only while each XCD
 // still runs at most one workgroup per compute unit: then the extra
 // workgroups land on idle units and each one's y and B share shrinks.
-void fused_feature_tiles(const Common& c, FusedArgs& a, int64_t rows, bool hostt)
+// uneven (the one-kernel launch with the host table): where that still
+// leaves compute units idle, the slices are cut into more, near-equal tiles
+// of whole 32-feature pairs, one more tile at a time for the slice whose
+// widest tile is widest, until each XCD runs one workgroup per compute unit
+// (decode QKV: Q in 10 tiles of 12-13 pairs and K, V in 3 of 10-11, i.e. 256
+// workgroups instead of 192 of 16 pairs).
+void fused_feature_tiles(const Common& c, FusedArgs& a, int64_t rows, bool hostt, bool uneven = false)
 {
     int F = a.F;
+    const int per_xcd = device_cus() / kXcds;
     if (c.t.feat <= 0) {
-        const int per_xcd = device_cus() / kXcds;
         while (F > 128) {
             int nf2 = 0;
             for (int sl = 0; sl < c.fs.n_s; ++sl)
@@ -2931,10 +2938,40 @@ void fused_feature_tiles(const Common& c, FusedArgs& a, int64_t rows, bool hostt
         set_fused_feat(c, a, F);
     }
     if (hostt) {
-        int ft = 0;
+        int n[4] = {0, 0, 0, 0}, tot = 0;
         for (int sl = 0; sl < c.fs.n_s; ++sl)
-            for (int i = 0; i < a.nft[sl]; ++i)
-                a.fts[ft++] = make_int2(sl, a.soff[sl] + i * a.F);
+            tot += n[sl] = a.nft[sl];
+        if (uneven && c.t.feat <= 0) {
+            const int64_t target = std::min<int64_t>(per_xcd / std::max<int64_t>(rows, 1), kFusedHostFt);
+            while (tot < target) {
+                int best = -1, widest = 1;
+                for (int sl = 0; sl < c.fs.n_s; ++sl) {
+                    const int p = c.fs.widths[sl] / 32, wmax = (p + n[sl] - 1) / n[sl];
+                    if (wmax > widest) {
+                        widest = wmax;
+                        best = sl;
+                    }
+                }
+                if (best < 0)
+                    break;  // every tile is one pair
+                ++n[best];
+                ++tot;
+            }
+        }
+        int ft = 0, most = 0;
+        for (int sl = 0; sl < c.fs.n_s; ++sl) {
+            const int p = c.fs.widths[sl] / 32;
+            int f = a.soff[sl];
+            for (int i = 0; i < n[sl]; ++i) {
+                const int pi = p / n[sl] + (i < p % n[sl] ? 1 : 0);
+                a.fts[ft++] = make_int2(sl | pi << 8, f);
+                f += 32 * pi;
+                most = std::max(most, pi);
+            }
+            a.nft[sl] = n[sl];
+        }
+        a.nf = ft;
+        a.F = 32 * most;
         for (; ft < kFusedHostFt; ++ft)
             a.fts[ft] = make_int2(0, 0);
     }
@@ -3038,7 +3075,7 @@ lora_status_t run_fused(const Common& c, const void* x, int64_t ldx, const void*
     bool hostt = c.r.kr && a.nf <= kFusedHostFt && fused_tile_table(c, a, rows);
     if (!hostt)
         rows = (tiles + kXcds - 1) / kXcds;
-    fused_feature_tiles(c, a, rows, hostt);
+    fused_feature_tiles(c, a, rows, hostt, true);
     // x through LDS when the wave's K range is one batch of 8 steps (K <= 4096)
     const bool xlds = a.wave_steps <= kXLdsSteps;
     const dim3 g((unsigned)(kXcds * a.nf), (unsigned)rows), blk(kFusedThreads);
