@@ -2019,17 +2019,17 @@ __device__ __forceinline__ void fused_expand_from_slabs(const FusedArgs& a, floa
     const int ftile = blockIdx.x / kXcds;
     const TileEntry te = a.tt[min(tile, kFusedHostTiles - 1)];
     const int2 fe = a.fts[min(ftile, kFusedHostFt - 1)];
-    const int sl = fe.x & 0xFF, f0 = fe.y;
+    const int sl = fe.x & 0xFF, f0 = fe.y, fw = 32 * (fe.x >> 8);
     const uint32_t live = te.n > 0 ? 1u : 0u;  // 0 for a padding tile
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, q = lane >> 4;
-    const int np = a.F >> 5;
+    const int np = fw >> 5;
     const bool tok = l16 < te.n;
     const RowMap<GATHER> rm{a.r.rows, te.t0, te.n, a.r.nrows};
     const uint32_t trow = rm(l16);
     const StreamBuf yb(rm.buf(a.y, a.ldy));  // y is read and written once: non-temporal
-    const Buf biasb(a.bias + (size_t)te.slot * a.out_f + f0, a.bias ? live * (uint32_t)(a.F * 2) : 0u);
-    const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(a.F * R * 2));
+    const Buf biasb(a.bias + (size_t)te.slot * a.out_f + f0, a.bias ? live * (uint32_t)(fw * 2) : 0u);
+    const Buf bb(a.B + ((size_t)te.slot * a.out_f + f0) * R, live * (uint32_t)(fw * R * 2));
     const int mrow = 8 * (l16 >> 2) + (l16 & 3);
     uint32_t yoff[NPAIR];
     // B fragments: lanes q < 2 fetch the rows of a pair's block 0 (the
@@ -3216,7 +3216,7 @@ lora_status_t run_splitk_short(const Common& c, const void* x, int64_t ldx, cons
     }
     if (b.nf > kFusedHostFt)
         return run_expand(c, a.slabs, slab, S, B_stack, bias, y, ldy, path, s);
-    fused_feature_tiles(c, b, rows, true);
+    fused_feature_tiles(c, b, rows, true, true);
     b.kc = 0;
     b.nsplit = S;
     const dim3 ge((unsigned)(kXcds * b.nf), (unsigned)rows);
