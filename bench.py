@@ -94,8 +94,9 @@ def parse():
                    help="print per-kernel means of the counters in rocprofv3 --pmc counter_collection.csv "
                         "files and the derived MFMA / VALU / L2 figures; needs no GPU")
     p.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "TRACE_CSV"), default=None,
-                   help="print the kernel table of a rocprofv3 --kernel-trace --stats -f csv run and the "
-                        "library's kernels split by launch grid; needs no GPU")
+                   help="print the kernel table of a rocprofv3 --kernel-trace --stats -f csv run, the "
+                        "library's kernels split by launch grid and, when the run also had --marker-trace "
+                        "(p_marker_api_trace.csv next to TRACE_CSV), by timed call kind; needs no GPU")
     return p.parse_args()
 
 
@@ -221,8 +222,14 @@ def trace_summary(stats_csv, trace_csv):
     """The kernel statistics of a rocprofv3 --kernel-trace --stats -f csv run
     (every dispatch of the run), then the library's kernels split by launch
     grid (workgroups x workgroup size), which separates the families and
-    call kinds that share one kernel instantiation."""
+    call kinds that share one kernel instantiation with different grids.
+    With the run's marker trace (--marker-trace: the marker_api_trace.csv
+    file beside trace_csv), also the library's dispatches inside each range
+    that the per-call timing opens around one call kind ("workload:kind"):
+    the per-kind figures that the bench line's avg_launch_us is measured on,
+    also where two call kinds share a kernel and a grid."""
     import csv
+    import glob
     import statistics
     from collections import defaultdict
     print(f"{'kernel':62s} {'calls':>8s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>8s}")
@@ -245,6 +252,30 @@ def trace_summary(stats_csv, trace_csv):
     print(f"{'kernel':62s} {'wgs':>6s} {'wg':>5s} {'calls':>7s} {'avg_us':>10s} {'median_us':>10s}")
     for (n, nwg, wg), d in sorted(grids.items(), key=lambda kv: -len(kv[1])):
         print(f"{n:62s} {nwg:6d} {wg:5d} {len(d):7d} {statistics.mean(d):10.2f} {statistics.median(d):10.2f}")
+    markers = sorted(glob.glob(os.path.join(os.path.dirname(os.path.abspath(trace_csv)), "*marker_api_trace.csv")))
+    if not markers:
+        return
+    ranges = []
+    with open(markers[0]) as fh:
+        for r in csv.DictReader(fh):
+            if ":" in r["Function"]:
+                ranges.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Function"]))
+    ranges.sort()
+    kinds = defaultdict(list)
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            if "lora::" not in r["Kernel_Name"]:
+                continue
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            hit = [name for (a, b, name) in ranges if a <= t0 and t1 <= b]
+            if hit:
+                kinds[(hit[-1], _short_kernel(r["Kernel_Name"]))].append((t1 - t0) / 1e3)
+    print()
+    print("Library kernels inside the per-call timing ranges (workload:call kind):")
+    print()
+    print(f"{'range':24s} {'kernel':62s} {'calls':>7s} {'avg_us':>10s} {'median_us':>10s}")
+    for (rng, n), d in sorted(kinds.items()):
+        print(f"{rng:24s} {n:62s} {len(d):7d} {statistics.mean(d):10.2f} {statistics.median(d):10.2f}")
 
 
 def cpu_identity() -> str:
@@ -520,6 +551,9 @@ def run_workload(args, torch, synth, srg, dev, log):
         spin = int(min(3.0 * enqueue_s / s_per_cycle + 1e5, 2e10))
         for _ in range(ev_reps):
             for kind in KINDS:
+                # a named range (ROCTX) around each timed sequence, so that a
+                # profiler's marker trace attributes its kernels to the kind
+                torch.cuda.nvtx.range_push(f"{args.workload}:{kind}")
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda._sleep(spin)
                 a.record()
@@ -530,6 +564,7 @@ def run_workload(args, torch, synth, srg, dev, log):
                         call(kind, ly)
                 b.record()
                 torch.cuda.synchronize()
+                torch.cuda.nvtx.range_pop()
                 total_ms[kind] += a.elapsed_time(b)
     avg_us = {k: 1e3 * total_ms[k] / (ev_reps * n_layers * (passes if k in kind_graphs else 1)) for k in KINDS}
     log("phase 2: " + " ".join(f"{k}={v:.2f}us" for k, v in avg_us.items()))

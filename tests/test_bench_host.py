@@ -76,3 +76,35 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert h["comments"] == h["base"]
     assert h["code"] != h["base"]
     assert h["string"] != h["base"]
+
+
+def test_trace_summary_attributes_dispatches_to_timing_ranges(tmp_path, capsys):
+    """Two call kinds that share a kernel and a grid are told apart by the
+    per-call timing ranges of the marker trace; dispatches outside every
+    range (the timed steps) and ranges without a 'workload:kind' name are
+    not attributed."""
+    import bench
+    name = "void lora::(anonymous namespace)::fused_delta_kernel<1, 8, true, true, false, 0>(lora::FusedArgs)"
+    with open(tmp_path / "p_kernel_stats.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writerow([name, 5, 35000, 7000, 100.0, 6000, 8000, 0])
+    cols = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Workgroup_Size_Y",
+            "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    rows = [(100, 108), (1000, 1007), (1010, 1017), (2000, 2006), (2010, 2016)]
+    with open(tmp_path / "p_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(cols)
+        for a, b in rows:
+            wr.writerow(["KERNEL_DISPATCH", name, a * 1000, b * 1000, 1024, 1, 1, 1024 * 128, 2, 1])
+    with open(tmp_path / "p_marker_api_trace.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Domain", "Function", "Process_Id", "Thread_Id", "Correlation_Id", "Start_Timestamp",
+                     "End_Timestamp"])
+        wr.writerow(["MARKER_CORE_RANGE_API", "decode:delta_qkv", 1, 1, 1, 990 * 1000, 1020 * 1000])
+        wr.writerow(["MARKER_CORE_RANGE_API", "decode:delta_o", 1, 1, 2, 1990 * 1000, 2020 * 1000])
+        wr.writerow(["MARKER_CORE_RANGE_API", "unrelated", 1, 1, 3, 0, 3000 * 1000])
+    bench.trace_summary(str(tmp_path / "p_kernel_stats.csv"), str(tmp_path / "p_kernel_trace.csv"))
+    out = capsys.readouterr().out
+    kinds = [ln.split() for ln in out.split("(workload:call kind):")[1].splitlines() if ln.startswith("decode:")]
+    assert [(k[0], k[-3], k[-2]) for k in kinds] == [("decode:delta_o", "2", "6.00"), ("decode:delta_qkv", "2", "7.00")]
