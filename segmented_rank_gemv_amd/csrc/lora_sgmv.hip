@@ -1053,6 +1053,95 @@ __device__ __forceinline__ void stage_u(const ExpandArgs& a, const TileInfo& ti,
     }
 }
 
+// stage_u for a rank R known at compile time (the MFMA expands), with the
+// same summation order.  The loads are batched so that a thread waits once
+// per slab, not once per slab and item: with one group (long tiles) the
+// slab loop is outside and each pass loads the thread's items of one slab
+// together (R / 16 of them for a full tile); with P groups each thread
+// loads up to four of its slabs at a time.  The generic version's loop
+// waited on every load before issuing the next, a chain of items x slabs
+// round trips for a full tile.
+template <int R>
+__device__ __forceinline__ void stage_u_r(const ExpandArgs& a, const TileInfo& ti, int ucol0, float* us,
+                                          float4* part)
+{
+    constexpr int r4 = R / 4;
+    constexpr int kItems = (kTileM * r4 + kThreads - 1) / kThreads;  // items of a thread in a full tile
+    const int NI = ti.n * r4;
+    const float* base = a.u + (size_t)ti.t0 * a.C + ucol0;
+    const int tid = threadIdx.x;
+    const int P = (a.S > 1 && 2 * NI <= kThreads) ? min(kThreads / NI, a.S) : 1;
+    if (P == 1) {
+        const float* src[kItems];
+        bool ok[kItems];
+        float4 acc[kItems];
+        // an item past the tile reads the tile's first row (the workgroup
+        // has at least one token) and is not stored: no branch between loads
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int e = tid + kThreads * k, i = e / r4, j = (e - i * r4) * 4;
+            ok[k] = e < NI;
+            src[k] = ok[k] ? base + (size_t)i * a.C + j : base;
+            acc[k] = *reinterpret_cast<const float4*>(src[k]);
+        }
+        for (int sl = 1; sl < a.S; ++sl) {
+            float4 v[kItems];
+#pragma unroll
+            for (int k = 0; k < kItems; ++k)
+                v[k] = *reinterpret_cast<const float4*>(src[k] + (size_t)sl * a.slab);
+#pragma unroll
+            for (int k = 0; k < kItems; ++k) {
+                acc[k].x += v[k].x;
+                acc[k].y += v[k].y;
+                acc[k].z += v[k].z;
+                acc[k].w += v[k].w;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int e = tid + kThreads * k, i = e / r4, j = (e - i * r4) * 4;
+            if (ok[k])
+                *reinterpret_cast<float4*>(us + i * R + j) = acc[k];
+        }
+        return;
+    }
+    if (tid < P * NI) {
+        const int e = tid % NI, g = tid / NI;
+        const int i = e / r4, j = (e - i * r4) * 4;
+        const float* p = base + (size_t)i * a.C + j;
+        float4 acc = *reinterpret_cast<const float4*>(p + (size_t)g * a.slab);
+        for (int sl = g + P; sl < a.S; sl += 4 * P) {
+            float4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)  // past the last slab: the last one again, not added
+                v[k] = *reinterpret_cast<const float4*>(p + (size_t)min(sl + k * P, a.S - 1) * a.slab);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (sl + k * P < a.S) {
+                    acc.x += v[k].x;
+                    acc.y += v[k].y;
+                    acc.z += v[k].z;
+                    acc.w += v[k].w;
+                }
+            }
+        }
+        part[g * NI + e] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < NI; e += kThreads) {
+        float4 acc = part[e];
+        for (int g = 1; g < P; ++g) {
+            const float4 v = part[g * NI + e];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const int i = e / r4, j = (e - i * r4) * 4;
+        *reinterpret_cast<float4*>(us + i * R + j) = acc;
+    }
+}
+
 // MFMA path (bf16).  Wave w owns tokens 16w .. 16w+15 of the tile and walks
 // the feature tile in pairs of 16-feature MFMA blocks.  For each 16 ranks one
 // v_mfma_f32_16x16x32_bf16 per block computes B·u with K = 32 = 16 ranks of
@@ -1175,7 +1264,7 @@ __device__ __forceinline__ void expand_mfma(const ExpandArgs& a, const TileInfo&
     }
     const uint4 bpiece = load_bias_piece(a, ti, f0);
     // u next: its loads go out before the wait on y and B
-    stage_u(a, ti, ucol0, us, part);
+    stage_u_r<R>(a, ti, ucol0, us, part);
 #pragma unroll
     for (int i = 0; i < kMaxPairs; ++i) {
         if (i < np) {
@@ -1294,7 +1383,7 @@ __device__ __forceinline__ void expand_mfma_lb(const ExpandArgs& a, const TileIn
         braw[i] = bb.ld16(p < a.ft * NCH ? (uint32_t)p * 16 : kOOB);
     }
     const uint4 bpiece = load_bias_piece(a, ti, f0);
-    stage_u(a, ti, ucol0, us, part);
+    stage_u_r<R>(a, ti, ucol0, us, part);
     store_bias_piece(a, bls, bpiece);
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
@@ -1398,7 +1487,7 @@ __device__ __forceinline__ void expand_mfma_reg(const ExpandArgs& a, const TileI
     }
     const uint4 bpiece = load_bias_piece(a, ti, f0);
 
-    stage_u(a, ti, ucol0, us, part);
+    stage_u_r<16 * NH>(a, ti, ucol0, us, part);
     store_bias_piece(a, bls, bpiece);
     __syncthreads();
     if (16 * w >= ti.n)
