@@ -368,7 +368,11 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  *                       16 to 64 with n_slices*R <= 64, slice widths
  *                       multiples of 64, host routing copy): -1 when the
  *                       batch fills the chip without splitting K (prefill-
- *                       sized batches), 0 never, 1 whenever it applies.
+ *                       sized batches) and either n_slices*R <= 16 or the
+ *                       call has no workspace of lora_sgmv_workspace_bytes
+ *                       (wider u otherwise takes the shrink and the expand
+ *                       in two launches, measured faster there), 0 never,
+ *                       1 whenever it applies.
  *   fused_max_tokens    AUTO takes the one-kernel path when no group has more
  *                       tokens than this (default 32; 0: never).
  *   splitk_short        on that path, the split-K form for an input width

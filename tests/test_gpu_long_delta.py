@@ -85,11 +85,12 @@ def test_long_delta_k_tail_and_short_last_wave():
 
 
 def test_prefill_auto_takes_the_long_delta():
-    """On the prefill workload AUTO runs with no workspace at all (only the
-    one-kernel paths accept that), so it takes the long delta there; the
-    result is bit-identical to the forced long delta and to the two-kernel
-    path (same K order and reduction tree in the shrink, same operand layout
-    in the expand), which does need the workspace."""
+    """On the prefill workload AUTO without a workspace takes the long delta
+    (only the one-kernel paths accept that); with one it takes the two-kernel
+    path for QKV (u of 48 columns) and the long delta for O (16).  Every
+    result is bit-identical to the forced long delta and to the forced
+    two-kernel path (same K order and reduction tree in the shrink, same
+    operand layout in the expand)."""
     w = synth.get_workload("prefill")
     lengths, slots = synth.draw_requests(w)
     ranks = synth.draw_ranks(w)
@@ -97,7 +98,8 @@ def test_prefill_auto_takes_the_long_delta():
     acts = synth.draw_activations(w, 1, int(lengths.sum()))
     ref = oracle_layer(w, stacks, lengths, slots, acts)
     ys = {}
-    for name, opts, ws in (("auto", None, False), ("long", LONG, False), ("two-kernel", NO_LONG, True)):
+    for name, opts, ws in (("auto", None, False), ("auto-ws", None, True), ("long", LONG, False),
+                           ("two-kernel", NO_LONG, True)):
         gl = GpuLayer(w, stacks, lengths, slots, acts)
         if not ws:
             gl.ws = {k: None for k in gl.ws}
@@ -106,7 +108,7 @@ def test_prefill_auto_takes_the_long_delta():
         log(f"[long] prefill {name} y_rel={ey:.3e}")
         assert ey <= TOL["bf16"], name
         ys[name] = (gl.y_arrival("y_qkv").view(np.uint32), gl.y_arrival("y_o").view(np.uint32))
-    for name in ("long", "two-kernel"):
+    for name in ("auto-ws", "long", "two-kernel"):
         assert np.array_equal(ys["auto"][0], ys[name][0]) and np.array_equal(ys["auto"][1], ys[name][1]), name
     gl = GpuLayer(w, stacks, lengths, slots, acts)
     gl.ws = {k: None for k in gl.ws}
