@@ -384,8 +384,8 @@ lora_status_t lora_sgmv_expand(const lora_dims_t* dims, int32_t family, const fl
  *   fused_k_rotation    staggered K ranges of the one-kernel path's waves:
  *                       -1 default (on), 0 off, 1 on.
  *   fold_slabs          two-kernel path: add the shrink's K-split partial
- *                       sums in a separate pass before the expand: -1 from
- *                       2048 LoRA-routed tokens, 0 never, 1 always. */
+ *                       sums in a separate pass before the expand: -1 or 0
+ *                       never (the expand adds them), 1 always. */
 typedef struct lora_options {
     int32_t long_delta;
     int32_t fused_max_tokens;

@@ -2537,12 +2537,8 @@ struct Tuning {
     int fold;          // -1 auto, 0 never, 1 always
 };
 
-// Longest group for which AUTO takes the one-kernel delta, and the LoRA
-// token count from which lora_sgmv_delta folds the shrink's slabs before the
-// expand (measured: Llama-3-8B prefill, 12.6 K tokens, -3 %; 3.6 K tokens,
-// -5 %; a 0.8 K-token mixed batch, +3 %).
+// Longest group for which AUTO takes the one-kernel delta.
 constexpr int kFusedMaxTokens = 32;
-constexpr int kDeltaFoldTokens = 2048;
 
 lora_status_t resolve_options(const lora_options_t* o, Tuning* t)
 {
@@ -3474,11 +3470,13 @@ lora_status_t run_delta(const Common& c, const void* x, int64_t ldx, const void*
         return st;
     int S = ch.S();
     const int64_t n4 = (int64_t)c.r.end * c.fs.C / 4;
-    // Fold the slabs into slab 0 first on long batches: every feature tile
-    // of the expand would otherwise read all S slabs of its token tile, while
-    // the fold reads them once, for one extra launch of a few microseconds
-    // that only a long batch amortises.  The fold_slabs option forces it.
-    if (S > 1 && (c.t.fold > 0 || (c.t.fold < 0 && c.r.end >= kDeltaFoldTokens))) {
+    // The fold_slabs option adds the slabs into slab 0 in a pass of its own
+    // first; by default every feature tile of the expand adds the S slabs of
+    // its token tile itself.  The fold paid on long batches while the
+    // expand's slab loop waited on every load (32-layer stack, 3.6 K tokens:
+    // -5 %); with the expand's batched slab loads it costs 1.7 % there (step
+    // 2.535 -> 2.578 ms) and is no longer taken by default.
+    if (S > 1 && c.t.fold > 0) {
         hipLaunchKernelGGL(reduce_slabs, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
                            0, s, slabs, n4, S, slabs, n4);
         if (hipGetLastError() != hipSuccess)

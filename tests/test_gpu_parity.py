@@ -58,9 +58,9 @@ def test_full_workload_parity(name, path, api):
     """split: lora_sgmv_shrink + lora_sgmv_expand (u checked too); delta:
     lora_sgmv_delta (AUTO takes the one-kernel path on decode batches);
     delta_reduce: lora_sgmv_delta on the two-kernel path with its slabs folded
-    by the reduce kernel before the expand (by default only batches of 2048
-    or more LoRA tokens fold); delta_nofold: the same path with the expand
-    reading every slab itself; split_devroute: split with the
+    by the reduce kernel before the expand (fold_slabs 1; by default no batch
+    folds); delta_nofold: the same path with the expand reading every slab
+    itself; split_devroute: split with the
     routing read from the device arrays only.  path fused: lora_sgmv_delta
     forced onto the one-kernel path."""
     w, lengths, slots, stacks, acts, ref = workload_case(name)
