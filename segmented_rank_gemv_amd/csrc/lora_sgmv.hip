@@ -2666,7 +2666,7 @@ void place_on_xcds(int n, const double* cost, int* order, int* xcd_of)
 // for all its tiles; the items are placed by their bytes (A range, x rows
 // and a fixed cost per workgroup).  With the plain order the column groups
 // of a tile fall on different XCDs and the tiles of a group on two (mixed
-// batch, hidden 5120, rank 64: shrink traffic 96 -> 66 MB per QKV call,
+// batch, hidden 5120, rank 64: shrink traffic 96 -> 70 MB per QKV call,
 // step 0.558 -> 0.545 ms; 32-layer stack 2.585 -> 2.572 ms).  Placing the
 // expand's workgroups the same way (all feature tiles of a tile on one XCD)
 // cut its traffic as well but ran slower (mixed 0.579 ms, stack 2.722 ms).
